@@ -1,0 +1,133 @@
+"""Tile orders of the pages' schedules, written from their prose.
+
+TEST INFRASTRUCTURE ONLY (see oracle/__init__.py). This module is the oracle's
+own statement of the schedules; the HIP library has its own, independent one,
+and the tests compare the two.
+
+Vocabulary
+----------
+A head's attention matrix is cut into n_q query (Q/dQ) tiles of BQ rows and
+n_kv key/value (KV) tiles of BKV rows, r = BKV / BQ (an integer >= 1), so
+n_q = r * n_kv. Tile (i, j) pairs Q tile i with KV tile j.
+
+An *item* is the ordered list of tiles one workgroup processes for one KV tile
+(or one pair of KV tiles), keeping that KV tile's dK/dV accumulators on chip:
+all work of one KV tile runs contiguously on one SM (DASH, zskr.cn explainer
+section 2.2; gist.science summary section 2.1, "Vincoli").
+
+The *accumulation order* of dQ tile i is the order in which the KV tiles' dQ
+partials are added into it. ``rank(i, j)`` is the position of KV tile j in it.
+
+Causal visibility: key position kv is visible from query position q iff
+kv <= q (same sequence for both), so tile (i, j) has at least one visible pair
+iff (i + 1) * BQ - 1 >= j * BKV, i.e. i >= j * r.
+"""
+from typing import Dict, List, Tuple
+
+SCHEDULES = ("serial_ascending", "descending_q", "shift", "symmetric_shift", "atomic_nondet")
+MASKS = ("full", "causal")
+
+Tile = Tuple[int, int]
+
+
+def tile_visible(i: int, j: int, r: int, causal: bool) -> bool:
+    return (not causal) or i >= j * r
+
+
+def column_rows(j: int, n_q: int, r: int, causal: bool) -> List[int]:
+    """Q tiles that interact with KV tile j, ascending."""
+    return [i for i in range(n_q) if tile_visible(i, j, r, causal)]
+
+
+def valid(schedule: str, mask: str, n_q: int, n_kv: int) -> bool:
+    """Shift is defined for full masks and symmetric shift for causal masks
+    (zskr.cn explainer sections 3.2 and 3.3; gist.science summary section 2.2B);
+    symmetric shift pairs KV tiles i and N-1-i, so it needs an even count."""
+    if schedule == "shift":
+        return mask == "full"
+    if schedule == "symmetric_shift":
+        return mask == "causal" and n_kv % 2 == 0
+    return schedule in SCHEDULES
+
+
+def items(schedule: str, mask: str, n_q: int, n_kv: int) -> List[List[Tile]]:
+    """Per-head items, each the list of tiles in visit order.
+
+    serial_ascending: KV tile j walks its Q tiles upward, the FA3 deterministic
+        baseline (zskr.cn section 2.1; gist.science section 1).
+    descending_q: the same loop reversed, Q tiles from the last down to the
+        first (zskr.cn section 3.1; gist.science section 2.2A).
+    atomic_nondet: ascending visits; order of dQ adds not fixed.
+    shift: the SM holding KV tile j starts at its own index and wraps around,
+        visiting j, j+1, ..., N-1, 0, ..., j-1 (zskr.cn section 3.2; gist.science
+        section 2.2B). With r > 1 Q tiles per KV tile the start is Q tile j*r.
+    symmetric_shift: KV tiles p and n_kv-1-p form one item. Phase 1 is a shift
+        over the dense lower-left rectangle (Q tiles in the bottom half, KV tiles
+        in the left half); phase 2 finishes column p above the rectangle,
+        ascending, then column n_kv-1-p, descending (zskr.cn section 3.3;
+        gist.science section 2.2B). The pages give no figure of the fold; this is
+        the plainest construction with one accumulator set live at a time.
+    """
+    causal = mask == "causal"
+    r = n_q // n_kv
+    assert r * n_kv == n_q and r >= 1, "BQ must divide BKV"
+    if not valid(schedule, mask, n_q, n_kv):
+        raise ValueError(f"{schedule} is not defined for mask {mask} with n_kv={n_kv}")
+    out: List[List[Tile]] = []
+    if schedule in ("serial_ascending", "atomic_nondet"):
+        for j in range(n_kv):
+            out.append([(i, j) for i in column_rows(j, n_q, r, causal)])
+    elif schedule == "descending_q":
+        for j in range(n_kv):
+            out.append([(i, j) for i in reversed(column_rows(j, n_q, r, causal))])
+    elif schedule == "shift":
+        for j in range(n_kv):
+            out.append([((j * r + t) % n_q, j) for t in range(n_q)])
+    elif schedule == "symmetric_shift":
+        half = n_q // 2
+        for p in range(n_kv // 2):
+            seq = [(half + (p * r + t) % half, p) for t in range(half)]
+            seq += [(i, p) for i in range(p * r, half)]
+            c = n_kv - 1 - p
+            seq += [(i, c) for i in range(n_q - 1, c * r - 1, -1)]
+            out.append(seq)
+    return out
+
+
+def accumulation_order(schedule: str, mask: str, n_q: int, n_kv: int) -> Dict[int, List[int]]:
+    """dQ tile i -> KV tiles in the order their partials are added.
+
+    serial_ascending and descending_q both keep FA3's ascending KV order; the
+    descending heuristic only reverses the loop that visits Q tiles (zskr.cn
+    section 3.1). For shift and symmetric shift, every item advances one tile
+    per step in lock step and the contributions to a dQ tile are added in step
+    order, which the pages describe as forming a natural dependency chain with
+    no conflicts (zskr.cn section 3.2; gist.science section 2.2B).
+    """
+    if schedule == "atomic_nondet":
+        raise ValueError("atomic_nondet has no fixed accumulation order")
+    causal = mask == "causal"
+    r = n_q // n_kv
+    order: Dict[int, List[int]] = {}
+    if schedule in ("serial_ascending", "descending_q"):
+        for i in range(n_q):
+            order[i] = [j for j in range(n_kv) if tile_visible(i, j, r, causal)]
+        return order
+    contrib: Dict[int, List[Tuple[int, int]]] = {i: [] for i in range(n_q)}
+    for seq in items(schedule, mask, n_q, n_kv):
+        for step, (i, j) in enumerate(seq):
+            contrib[i].append((step, j))
+    for i, lst in contrib.items():
+        steps = [s for s, _ in lst]
+        assert len(set(steps)) == len(steps), f"two contributions to dQ tile {i} at one step"
+        order[i] = [j for _, j in sorted(lst)]
+    return order
+
+
+def rank_table(schedule: str, mask: str, n_q: int, n_kv: int) -> Dict[Tile, int]:
+    """(i, j) -> position of KV tile j in dQ tile i's accumulation order."""
+    out: Dict[Tile, int] = {}
+    for i, js in accumulation_order(schedule, mask, n_q, n_kv).items():
+        for pos, j in enumerate(js):
+            out[(i, j)] = pos
+    return out

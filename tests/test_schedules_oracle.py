@@ -1,0 +1,87 @@
+"""Pins of the oracle's schedule definitions: golden n = 4 tables, exact coverage,
+conflict-free steps, and the pages' load-balance claims."""
+import json
+import os
+
+import pytest
+
+from oracle import schedules as S
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "schedules_n4.json")))
+
+
+def test_golden_shift_n4():
+    g = GOLDEN["shift_full"]
+    its = S.items("shift", "full", 4, 4)
+    assert [[i for i, _ in it] for it in its] == g["visits_q_tiles_per_kv_tile"]
+    assert {str(k): v for k, v in S.accumulation_order("shift", "full", 4, 4).items()} == g["dq_order"]
+
+
+def test_golden_symmetric_n4():
+    g = GOLDEN["symmetric_shift_causal"]
+    its = S.items("symmetric_shift", "causal", 4, 4)
+    assert [[list(t) for t in it] for it in its] == g["items_tiles_q_kv"]
+    assert all(len(it) == g["tiles_per_item"] for it in its)
+    assert {str(k): v for k, v in S.accumulation_order("symmetric_shift", "causal", 4, 4).items()} == g["dq_order"]
+
+
+@pytest.mark.parametrize("name,sched", [("serial_ascending_causal", "serial_ascending"),
+                                        ("descending_q_causal", "descending_q")])
+def test_golden_serial_and_descending_n4(name, sched):
+    g = GOLDEN[name]
+    its = S.items(sched, "causal", 4, 4)
+    assert [[i for i, _ in it] for it in its] == g["visits_q_tiles_per_kv_tile"]
+    assert {str(k): v for k, v in S.accumulation_order(sched, "causal", 4, 4).items()} == g["dq_order"]
+
+
+CASES = [(n_kv, r) for n_kv in (2, 4, 6, 8, 16) for r in (1, 2, 4)]
+
+
+@pytest.mark.parametrize("n_kv,r", CASES)
+@pytest.mark.parametrize("sched,mask", [("serial_ascending", "full"), ("serial_ascending", "causal"),
+                                        ("descending_q", "full"), ("descending_q", "causal"),
+                                        ("shift", "full"), ("symmetric_shift", "causal"),
+                                        ("atomic_nondet", "full"), ("atomic_nondet", "causal")])
+def test_exact_once_coverage(sched, mask, n_kv, r):
+    n_q = n_kv * r
+    its = S.items(sched, mask, n_q, n_kv)
+    seen = [t for it in its for t in it]
+    want = [(i, j) for i in range(n_q) for j in range(n_kv) if S.tile_visible(i, j, r, mask == "causal")]
+    assert sorted(seen) == sorted(want) and len(seen) == len(set(seen))
+
+
+@pytest.mark.parametrize("n_kv,r", CASES)
+def test_shift_and_symmetric_are_conflict_free(n_kv, r):
+    # At every lock-step the items touch pairwise distinct dQ tiles, so no item ever
+    # has to wait for a concurrent one (zskr.cn 3.2 'conflict-free reduction').
+    n_q = n_kv * r
+    for sched, mask in (("shift", "full"), ("symmetric_shift", "causal")):
+        its = S.items(sched, mask, n_q, n_kv)
+        L = len(its[0])
+        assert all(len(it) == L for it in its), "unequal item lengths break the lock step"
+        for t in range(L):
+            rows = [it[t][0] for it in its]
+            assert len(set(rows)) == len(rows), (sched, t, rows)
+
+
+@pytest.mark.parametrize("n_kv,r", CASES)
+def test_symmetric_items_are_balanced(n_kv, r):
+    # Folding the triangle into a rectangle: every pair holds n_q + r tiles (r = 1: N + 1).
+    n_q = n_kv * r
+    its = S.items("symmetric_shift", "causal", n_q, n_kv)
+    assert all(len(it) == n_q + r for it in its)
+    for p, it in enumerate(its):
+        assert {j for _, j in it} == {p, n_kv - 1 - p}
+
+
+def test_descending_keeps_the_ascending_dq_order():
+    for mask in ("full", "causal"):
+        assert S.accumulation_order("descending_q", mask, 8, 4) == S.accumulation_order("serial_ascending", mask, 8, 4)
+
+
+def test_invalid_pairs():
+    assert not S.valid("shift", "causal", 8, 8)
+    assert not S.valid("symmetric_shift", "full", 8, 8)
+    assert not S.valid("symmetric_shift", "causal", 5, 5)
+    with pytest.raises(ValueError):
+        S.items("shift", "causal", 4, 4)
