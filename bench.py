@@ -1,0 +1,211 @@
+"""Throughput of the deterministic attention backward on one MI355X.
+
+Workload: causal attention backward, B=1, H=32, S=8192, D=128, bf16 inputs
+drawn from N(0,1) (seeded), O and LSE from the library's forward. One step is
+one attn_bwd_deterministic call (preprocess D = rowsum(dO*O), main kernel,
+dQ convert) with all inputs resident in HBM. Counted FLOPs per step follow the
+usual attention-backward convention, 10*B*H*S^2*D, halved for causal.
+
+Prints one JSON line. Progress goes to stderr.
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+CONFIGS = {
+    # name: (B, H, S, D, causal, seed)
+    "causal_b1_h32_s8192_d128": (1, 32, 8192, 128, True, 104),
+    "full_b2_h32_s4096_d128": (2, 32, 4096, 128, False, 103),
+    "causal_b4_h16_s2048_d64": (4, 16, 2048, 64, True, 102),
+    "full_b1_h16_s16384_d128": (1, 16, 16384, 128, False, 105),
+    "causal_b1_h16_s16384_d128": (1, 16, 16384, 128, True, 105),
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles, so the library can record them around its main kernel."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, e):
+        self.hip.hipEventDestroy(e)
+
+
+def counted_flops(B, H, S, D, causal):
+    f = 10.0 * B * H * S * S * D
+    return f / 2 if causal else f
+
+
+def tiles_executed(plan, B, H, causal):
+    n_q, n_kv, r = plan["n_q"], plan["n_kv"], plan["block_kv"] // plan["block_q"]
+    per_head = sum((n_q - j * r) if causal else n_q for j in range(n_kv))
+    return B * H * per_head
+
+
+def time_schedule(da, torch, ev, tensors, shape, causal, sched, steps, warmup):
+    q, k, v, o, do, lse = tensors
+    B, H, S, D = shape
+    ws = da.alloc_workspace(B, H, S, D)
+    out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    for _ in range(warmup):
+        da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule=sched, workspace=ws, out=out)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in out]
+    begins = [ev.create() for _ in range(steps)]
+    ends = [ev.create() for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for s in range(steps):
+        da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule=sched, workspace=ws, out=out,
+                                  main_begin_event=begins[s], main_end_event=ends[s])
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    main_ms = [ev.elapsed_ms(b, e) for b, e in zip(begins, ends)]
+    for e in begins + ends:
+        ev.destroy(e)
+    status = da.detattn_device_status(ws)
+    same = all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(ref, out))
+    return {"ms_per_step": total_ms / steps, "main_ms": sum(main_ms) / steps, "status": status,
+            "repeat_bitwise": bool(same)}
+
+
+def cpu_baseline(cfg_shape, causal, seed, budget_s=15.0, max_heads=64):
+    """The fp64 oracle (unchanged) on whole heads of the same workload until ~budget_s of CPU time."""
+    import torch
+
+    from deterministic_attention_backward_fa_amd.synth import make_qkvdo
+    from oracle import ref
+
+    B, H, S, D = cfg_shape
+    q, k, v, do = make_qkvdo(B, H, S, D, seed)
+    scale = 1.0 / math.sqrt(D)
+    heads, elapsed = 0, 0.0
+    while heads < min(max_heads, B * H) and elapsed < budget_s:
+        b, h = divmod(heads, H)
+        sl = [t[b:b + 1, h:h + 1] for t in (q, k, v, do)]
+        t0 = time.perf_counter()
+        ref.attn_bwd(*sl, scale, causal)
+        elapsed += time.perf_counter() - t0
+        heads += 1
+        log(f"[cpu_baseline] oracle head {heads}: {elapsed:.1f} s cumulative")
+    flops = counted_flops(1, heads, S, D, causal)
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": ref.max_threads(), "kind": "oracle",
+            "sample": f"fp64 oracle backward (forward statistics recomputed) on {heads} of {B * H} heads "
+                      f"(S={S}, D={D}, {'causal' if causal else 'full'}), {elapsed:.1f} s wall",
+            "seconds": elapsed}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="causal_b1_h32_s8192_d128", choices=sorted(CONFIGS))
+    ap.add_argument("--schedule", default=None, help="headline schedule (default: shift / symmetric_shift)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-headline", action="store_true", help="skip the other schedules")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import deterministic_attention_backward_fa_amd as da
+    from deterministic_attention_backward_fa_amd.synth import make_qkvdo
+
+    B, H, S, D, causal, seed = CONFIGS[args.config]
+    headline = args.schedule or ("symmetric_shift" if causal else "shift")
+    log(f"[bench] {args.config}: generating inputs (seed {seed})")
+    q, k, v, do = (t.cuda() for t in make_qkvdo(B, H, S, D, seed))
+    o, lse = da.detattn_fwd(q, k, v, causal=causal)
+    torch.cuda.synchronize()
+    tensors = (q, k, v, o, do, lse)
+    ev = HipEvents()
+    scheds = [headline]
+    if not args.only_headline:
+        scheds += [s for s in (["serial_ascending", "descending_q"] +
+                               (["symmetric_shift"] if causal else ["shift"]) + ["atomic_nondet"]) if s != headline]
+    flops = counted_flops(B, H, S, D, causal)
+    results = {}
+    for sched in scheds:
+        log(f"[bench] timing {sched}: warmup {args.warmup}, steps {args.steps}")
+        r = time_schedule(da, torch, ev, tensors, (B, H, S, D), causal, sched, args.steps, args.warmup)
+        r["tflops"] = flops / (r["ms_per_step"] * 1e-3) / 1e12
+        results[sched] = r
+        log(f"[bench] {sched}: {r['ms_per_step']:.3f} ms/step, main {r['main_ms']:.3f} ms, "
+            f"{r['tflops']:.1f} TFLOP/s, status {r['status']}, repeat bitwise {r['repeat_bitwise']}")
+    head = results[headline]
+    plan = da.detattn_bwd_plan(B, H, S, D, causal, headline)
+    tiles = tiles_executed(plan, B, H, causal)
+    algo_flops = 10.0 * plan["block_q"] * plan["block_kv"] * D * tiles
+    achieved = algo_flops / (head["main_ms"] * 1e-3) / 1e12
+    atomic = results.get("atomic_nondet")
+    line = {
+        "metric": "deterministic attn-bwd TFLOP/s (bf16, full+causal) and ratio vs atomic nondet",
+        "value": round(head["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{'causal' if causal else 'full'} attention backward B={B} H={H} S={S} D={D}",
+                   "schedule": headline, "block_q": plan["block_q"], "block_kv": plan["block_kv"],
+                   "grid": plan["grid"], "parallelism": "single GPU"},
+        "ratio_vs_atomic": round(head["tflops"] / atomic["tflops"], 4) if atomic else None,
+        "schedules": {s: {"tflops": round(r["tflops"], 2), "ms_per_step": round(r["ms_per_step"], 4),
+                          "main_ms": round(r["main_ms"], 4), "repeat_bitwise": r["repeat_bitwise"],
+                          "ratio_vs_atomic": round(r["tflops"] / atomic["tflops"], 4) if atomic else None}
+                      for s, r in results.items()},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "bwd_main_kernel", "algorithmic_flops_per_launch": algo_flops,
+                     "avg_launch_ms": round(head["main_ms"], 4)},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline: fp64 oracle on a bounded sample")
+        line["cpu_baseline"] = cpu_baseline((B, H, S, D), causal, seed)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

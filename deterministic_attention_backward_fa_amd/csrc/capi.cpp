@@ -1,0 +1,321 @@
+// C ABI of libdetattn (declared in include/detattn.h): argument validation,
+// tile and grid planning, workspace carving and kernel launches.
+#include "detattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "launch.h"
+#include "tile_sched.h"
+
+using namespace detattn;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool shape_ok(const detattn_shape_t& s) {
+  if (s.B < 0 || s.H < 0 || s.S < 0 || s.D <= 0) return false;
+  const long long n = (long long)s.B * s.H * s.S * s.D;
+  return n < (1LL << 31);
+}
+
+bool is_empty(const detattn_shape_t& s) { return s.B == 0 || s.H == 0 || s.S == 0; }
+
+// Library tile choice per head dimension and length: the KV tile (BKV rows,
+// owned by one workgroup) and the Q tile (BQ rows, one sweep step).
+void default_tiles(int D, int S, int& bq, int& bkv) {
+  if (D == 64) {
+    if (S % 128 == 0 && S >= 512) {
+      bq = 128;
+      bkv = 128;
+    } else {
+      bq = 64;
+      bkv = 64;
+    }
+  } else {
+    if (S >= 16384 || S % 128 != 0) {
+      bq = 64;
+      bkv = 64;
+    } else {
+      bq = 64;
+      bkv = 128;
+    }
+  }
+}
+
+bool tiles_built(int D, int bq, int bkv) {
+  if (D == 64) return (bq == 64 && bkv == 64) || (bq == 128 && bkv == 128) || (bq == 64 && bkv == 128);
+  if (D == 128) return (bq == 64 && bkv == 128) || (bq == 64 && bkv == 64);
+  return false;
+}
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return cus;
+}
+
+struct Plan {
+  detattn_plan_t pub;
+  int causal, sch, dqm_internal, xcd;
+  long long timeout_ticks;
+};
+
+int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t sch, const detattn_bwd_options_t* opt,
+              Plan& P) {
+  if (!shape_ok(s) || is_empty(s)) return DETATTN_ERR_INVALID_ARG;
+  if (mask != DETATTN_MASK_FULL && mask != DETATTN_MASK_CAUSAL) return DETATTN_ERR_INVALID_ARG;
+  if ((int)sch < 0 || (int)sch > 4) return DETATTN_ERR_INVALID_ARG;
+  if (s.D != 64 && s.D != 128) return DETATTN_ERR_UNSUPPORTED;
+  detattn_bwd_options_t o;
+  std::memset(&o, 0, sizeof(o));
+  if (opt) o = *opt;
+  if (o.block_q < 0 || o.block_kv < 0 || o.grid < 0 || o.xcd_remap < 0 || o.xcd_remap > 2 || o.dq_mode < 0 ||
+      o.dq_mode > 2)
+    return DETATTN_ERR_INVALID_ARG;
+  int bq, bkv;
+  default_tiles(s.D, s.S, bq, bkv);
+  if (o.block_q) bq = o.block_q;
+  if (o.block_kv) bkv = o.block_kv;
+  if (!tiles_built(s.D, bq, bkv)) return DETATTN_ERR_UNSUPPORTED;
+  if (s.S % bq != 0 || s.S % bkv != 0) return DETATTN_ERR_UNSUPPORTED;
+  const int causal = mask == DETATTN_MASK_CAUSAL;
+  const int n_q = s.S / bq, n_kv = s.S / bkv, r = bkv / bq;
+  if (sch == DETATTN_SHIFT && causal) return DETATTN_ERR_UNSUPPORTED;
+  if (sch == DETATTN_SYMMETRIC_SHIFT && (!causal || n_kv % 2 != 0)) return DETATTN_ERR_UNSUPPORTED;
+
+  int dqm = kDqUnordered;
+  int pub_dqm = 0;
+  if (sch != DETATTN_ATOMIC_NONDET) {
+    pub_dqm = o.dq_mode ? o.dq_mode : DETATTN_DQ_ORDERED_RMW;
+    dqm = pub_dqm == DETATTN_DQ_ORDERED_ATOMIC ? kDqOrderedAtomic : kDqOrderedRmw;
+  }
+  const MainInfo info = s.D == 64 ? main_info_d64(bq, bkv, causal, dqm) : main_info_d128(bq, bkv, causal, dqm);
+  if (!info.func) return DETATTN_ERR_UNSUPPORTED;
+
+  const Sched sc{(int)sch, causal, n_q, n_kv, r};
+  const long long BH = (long long)s.B * s.H;
+  const long long items = BH * sc.items_per_head();
+  int capacity = 0;  // co-resident workgroups
+  if (o.grid == 0) {
+    const int cus = device_cus();
+    if (cus <= 0 || info.occupancy <= 0) return DETATTN_ERR_HIP;
+    capacity = cus * info.occupancy;
+  }
+  const bool ring_sched = (sch == DETATTN_SHIFT || sch == DETATTN_SYMMETRIC_SHIFT);
+  int grid = o.grid ? o.grid : capacity;
+  int ring = 0, rings = 0;
+  int xcd = o.xcd_remap != 2;
+  if (ring_sched) {
+    // Every ring (the items of one head) must be co-resident. With the XCD
+    // remap a ring occupies consecutive slots of one XCD (workgroup w runs on
+    // XCD w % 8), so its dQ hand-offs stay inside that XCD's L2.
+    ring = sc.items_per_head();
+    if (grid < ring) return DETATTN_ERR_UNSUPPORTED;
+    if (xcd && grid % 8 == 0 && ring <= grid / 8) {
+      long long per_xcd = (grid / 8) / ring;
+      const long long need = (BH + 7) / 8;
+      if (per_xcd > need) per_xcd = need;
+      rings = (int)(8 * per_xcd);
+    } else {
+      xcd = 0;
+      rings = grid / ring;
+      if ((long long)rings > BH) rings = (int)BH;
+    }
+    grid = rings * ring;
+  } else {
+    if ((long long)grid > items) grid = (int)items;
+  }
+  P.pub.block_q = bq;
+  P.pub.block_kv = bkv;
+  P.pub.n_q = n_q;
+  P.pub.n_kv = n_kv;
+  P.pub.items = (int32_t)items;
+  P.pub.grid = grid;
+  P.pub.ring = ring;
+  P.pub.rings = rings;
+  P.pub.dq_mode = pub_dqm;
+  P.pub.cooperative = ring_sched ? 1 : 0;
+  P.causal = causal;
+  P.sch = (int)sch;
+  P.dqm_internal = dqm;
+  P.xcd = xcd;
+  const long long us = o.timeout_us ? (long long)o.timeout_us : 4000000LL;
+  P.timeout_ticks = us * 100;  // s_memrealtime runs at 100 MHz
+  return DETATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* detattn_status_string(int status) {
+  switch (status) {
+    case DETATTN_OK: return "ok";
+    case DETATTN_ERR_INVALID_ARG: return "invalid argument";
+    case DETATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DETATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case DETATTN_ERR_HIP: return "HIP runtime error";
+    case DETATTN_ERR_DEVICE_TIMEOUT: return "ordered dQ wait timed out on the device";
+    default: return "unknown status";
+  }
+}
+
+size_t detattn_bwd_workspace_bytes(detattn_shape_t s, detattn_mask_t mask, detattn_schedule_t schedule) {
+  (void)mask;
+  (void)schedule;
+  if (!shape_ok(s)) return 0;
+  WsLayout L((long long)s.B * s.H, s.S, s.D);
+  return L.total;
+}
+
+int detattn_bwd_plan(detattn_shape_t shape, detattn_mask_t mask, detattn_schedule_t schedule,
+                     const detattn_bwd_options_t* options, detattn_plan_t* plan) {
+  if (!plan) return DETATTN_ERR_INVALID_ARG;
+  Plan P;
+  const int st = make_plan(shape, mask, schedule, options, P);
+  if (st == DETATTN_OK) *plan = P.pub;
+  return st;
+}
+
+int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                              const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                              size_t workspace_bytes, detattn_shape_t s, detattn_mask_t mask,
+                              detattn_schedule_t schedule, const detattn_bwd_options_t* options, void* stream) {
+  if (!shape_ok(s)) return DETATTN_ERR_INVALID_ARG;
+  if (mask != DETATTN_MASK_FULL && mask != DETATTN_MASK_CAUSAL) return DETATTN_ERR_INVALID_ARG;
+  if ((int)schedule < 0 || (int)schedule > 4) return DETATTN_ERR_INVALID_ARG;
+  if (is_empty(s)) return DETATTN_OK;
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return DETATTN_ERR_INVALID_ARG;
+  Plan P;
+  const int st = make_plan(s, mask, schedule, options, P);
+  if (st != DETATTN_OK) return st;
+  const long long BH = (long long)s.B * s.H;
+  WsLayout L(BH, s.S, s.D);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < L.total)
+    return DETATTN_ERR_WORKSPACE;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  unsigned* header = reinterpret_cast<unsigned*>(ws);
+  int* flags = reinterpret_cast<int*>(ws + L.flags_off);
+  float* delta = reinterpret_cast<float*>(ws + L.delta_off);
+  float* dqacc = reinterpret_cast<float*>(ws + L.dqacc_off);
+  hipStream_t st_ = static_cast<hipStream_t>(stream);
+  const long long rows = BH * s.S;
+  const long long elems = rows * s.D;
+  const bool unordered = P.dqm_internal == kDqUnordered;
+
+  hipError_t e = launch_pre(s.D, static_cast<const __bf16*>(o), static_cast<const __bf16*>(dout), delta, rows, flags,
+                            BH * P.pub.n_q, header, unordered ? dqacc : nullptr, elems, st_);
+  if (e != hipSuccess) return DETATTN_ERR_HIP;
+
+  MainLaunch M;
+  std::memset(&M, 0, sizeof(M));
+  BwdArgs& a = M.args;
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.dout = static_cast<const __bf16*>(dout);
+  a.lse = lse;
+  a.delta = delta;
+  a.dqacc = dqacc;
+  a.dk = static_cast<__bf16*>(dk);
+  a.dv = static_cast<__bf16*>(dv);
+  a.flags = flags;
+  a.ticket = header;
+  a.err = header + 16;
+  a.BH = (int)BH;
+  a.S = s.S;
+  a.scale = s.softmax_scale;
+  a.sc = Sched{P.sch, P.causal, P.pub.n_q, P.pub.n_kv, P.pub.block_kv / P.pub.block_q};
+  a.ticket_mode = P.pub.ring == 0;
+  a.ring = P.pub.ring;
+  a.rings = P.pub.rings;
+  a.xcd_remap = P.xcd;
+  a.timeout_ticks = P.timeout_ticks;
+  a.delay_seed = options ? options->debug_delay_seed : 0u;
+  a.skip_item = (options && options->debug_skip_signal > 0) ? options->debug_skip_signal - 1 : -1;
+  M.D = s.D;
+  M.BQ = P.pub.block_q;
+  M.BKV = P.pub.block_kv;
+  M.causal = P.causal;
+  M.dq_mode = P.dqm_internal;
+  M.grid = P.pub.grid;
+  M.cooperative = P.pub.cooperative;
+  if (options && options->main_begin_event &&
+      hipEventRecord(static_cast<hipEvent_t>(options->main_begin_event), st_) != hipSuccess)
+    return DETATTN_ERR_HIP;
+  e = launch_main(M, st_);
+  if (e == hipSuccess && options && options->main_end_event)
+    e = hipEventRecord(static_cast<hipEvent_t>(options->main_end_event), st_);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return e == hipErrorCooperativeLaunchTooLarge ? DETATTN_ERR_UNSUPPORTED : DETATTN_ERR_HIP;
+  }
+  e = launch_convert(dqacc, static_cast<__bf16*>(dq), elems, s.softmax_scale, st_);
+  return e == hipSuccess ? DETATTN_OK : DETATTN_ERR_HIP;
+}
+
+int attn_bwd_deterministic(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                           detattn_shape_t shape, detattn_mask_t mask, detattn_schedule_t schedule, void* stream) {
+  return attn_bwd_deterministic_ex(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, shape, mask,
+                                   schedule, nullptr, stream);
+}
+
+int detattn_device_status(void* workspace, void* stream) {
+  if (!workspace) return DETATTN_ERR_INVALID_ARG;
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return DETATTN_ERR_HIP;
+  unsigned err = 0;
+  const unsigned* header = static_cast<const unsigned*>(workspace);
+  if (hipMemcpy(&err, header + 16, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess) return DETATTN_ERR_HIP;
+  return err == kErrNone ? DETATTN_OK : DETATTN_ERR_DEVICE_TIMEOUT;
+}
+
+int detattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, detattn_shape_t s,
+                detattn_mask_t mask, void* stream) {
+  if (!shape_ok(s)) return DETATTN_ERR_INVALID_ARG;
+  if (mask != DETATTN_MASK_FULL && mask != DETATTN_MASK_CAUSAL) return DETATTN_ERR_INVALID_ARG;
+  if (is_empty(s)) return DETATTN_OK;
+  const void* ptrs[] = {q, k, v, o, lse};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return DETATTN_ERR_INVALID_ARG;
+  if (s.D != 64 && s.D != 128) return DETATTN_ERR_UNSUPPORTED;
+  if (s.S % 128 != 0) return DETATTN_ERR_UNSUPPORTED;
+  hipError_t e = launch_fwd(s.D, mask == DETATTN_MASK_CAUSAL, static_cast<const __bf16*>(q),
+                            static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse,
+                            s.B * s.H, s.S, s.softmax_scale, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DETATTN_OK : DETATTN_ERR_HIP;
+}
+
+int detattn_schedule_items_per_head(int32_t schedule, int32_t mask, int32_t n_q, int32_t n_kv) {
+  if (schedule < 0 || schedule > 4 || (mask != 0 && mask != 1) || n_q <= 0 || n_kv <= 0 || n_q % n_kv != 0)
+    return -1;
+  if (schedule == kShift && mask != 0) return -1;
+  if (schedule == kSymmetricShift && (mask != 1 || n_kv % 2 != 0)) return -1;
+  const Sched sc{schedule, mask, n_q, n_kv, n_q / n_kv};
+  return sc.items_per_head();
+}
+
+int detattn_schedule_item(int32_t schedule, int32_t mask, int32_t n_q, int32_t n_kv, int32_t item, int32_t* q_tiles,
+                          int32_t* kv_tiles, int32_t* ranks, int32_t cap) {
+  const int ip = detattn_schedule_items_per_head(schedule, mask, n_q, n_kv);
+  if (ip < 0 || item < 0 || item >= ip || cap < 0) return -1;
+  const Sched sc{schedule, mask, n_q, n_kv, n_q / n_kv};
+  const int len = sc.item_len(item);
+  for (int t = 0; t < len && t < cap; ++t) {
+    int i, j;
+    sc.tile(item, t, i, j);
+    if (q_tiles) q_tiles[t] = i;
+    if (kv_tiles) kv_tiles[t] = j;
+    if (ranks) ranks[t] = schedule == kAtomicNondet ? -1 : sc.rank(i, j);
+  }
+  return len;
+}
+
+}  // extern "C"

@@ -1,0 +1,134 @@
+// Device helpers shared by the gfx950 kernels: bf16 vectors, MFMA wrappers,
+// LDS transpose reads and the workspace layout.
+//
+// MFMA lane layouts (v_mfma_f32_32x32x16_bf16, wave64), with l = lane id,
+// g = l / 32:
+//   A (32 x 16, M x K): lane l holds A[l % 32][8g .. 8g+7]
+//   B (16 x 32, K x N): lane l holds B[8g .. 8g+7][l % 32]
+//   C (32 x 32):        lane l, register r holds C[8(r/4) + 4g + r%4][l % 32]
+// Since A and B are both "8 contiguous K values for one fixed non-K index",
+// a C tile can feed the next product as either operand with its *row* index
+// as the contraction index, provided the other operand uses the same
+// permutation of K: lane group g then holds rows {4g..4g+3, 8+4g..8+4g+3} of
+// each 16-row slice (registers 8h..8h+7 of the accumulator for slice h).
+//
+// ds_read_b64_tr_b16 (gfx950) works on groups of 16 lanes: output lane i,
+// element t receives element (i & 3) of the 64-bit word addressed by lane
+// 4t + (i >> 2) of its group. If lane s of a group addresses row k0 + s/4,
+// columns c0 + 4(s%4) .. +3 of a row-major bf16 matrix M, output lane i gets
+// M[k0 .. k0+3][c0 + i]: a 4 x 16 block read transposed. Two such reads give
+// the 8 K values an MFMA operand lane needs from a matrix stored K-major.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace detattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+static constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
+
+__device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) {
+  bf16x4 r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  r[2] = (__bf16)c;
+  r[3] = (__bf16)d;
+  return r;
+}
+
+// Eight accumulator registers [8h, 8h+8) of a C tile as a bf16 MFMA operand.
+__device__ __forceinline__ bf16x8 acc_slice_bf16(const f32x16& c, int h) {
+  bf16x8 r;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) r[t] = (__bf16)c[8 * h + t];
+  return r;
+}
+
+// 16-byte LDS load/store.
+__device__ __forceinline__ bf16x8 lds_load16(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ void lds_store16(__bf16* p, const bf16x8& v) { *reinterpret_cast<bf16x8*>(p) = v; }
+
+// Transposed 4x16 read (see header): `p` is this lane's 64-bit source address.
+__device__ __forceinline__ bf16x4 lds_read_tr(const __bf16* p) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 cat(const bf16x4& a, const bf16x4& b) {
+  bf16x8 r;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    r[t] = a[t];
+    r[4 + t] = b[t];
+  }
+  return r;
+}
+
+// Operand fragment of a row-major bf16 matrix M (pitch in elements), read
+// K-major: lane holds M[k0 + rows(g)][c0 + l%32] for the 8 K rows its group
+// needs. `perm` selects the accumulator-compatible K permutation
+// ({4g..4g+3, 8+4g..8+4g+3}); otherwise K rows 8g..8g+7 in order.
+__device__ __forceinline__ bf16x8 frag_tr(const __bf16* M, int pitch, int k0, int c0, bool perm) {
+  const int l = threadIdx.x & 63;
+  const int s = l & 15;           // lane within its 16-lane group
+  const int grp = l >> 4;         // 0..3
+  const int g = grp >> 1;         // K half
+  const int cbase = c0 + 16 * (grp & 1) + 4 * (s & 3);
+  int ka, kb;
+  if (perm) {
+    ka = k0 + 4 * g + (s >> 2);
+    kb = ka + 8;
+  } else {
+    ka = k0 + 8 * g + (s >> 2);
+    kb = ka + 4;
+  }
+  bf16x4 lo = lds_read_tr(M + ka * pitch + cbase);
+  bf16x4 hi = lds_read_tr(M + kb * pitch + cbase);
+  return cat(lo, hi);
+}
+
+// Operand fragment of a row-major bf16 matrix read along its rows: lane holds
+// M[r0 + l%32][k0 + 8g .. +7].
+__device__ __forceinline__ bf16x8 frag_row(const __bf16* M, int pitch, int r0, int k0) {
+  const int l = threadIdx.x & 63;
+  return lds_load16(M + (r0 + (l & 31)) * pitch + k0 + 8 * (l >> 5));
+}
+
+// Workspace layout (all offsets in bytes from the workspace base).
+struct WsLayout {
+  static constexpr size_t kHeader = 256;         // ticket @0, error word @64, error detail @128
+  static constexpr size_t kFlagStride = 128;     // one L2 line per dQ tile flag
+  static constexpr size_t kMinBlockQ = 64;
+  size_t flags_off, flags_bytes, delta_off, delta_bytes, dqacc_off, dqacc_bytes, total;
+  __host__ __device__ WsLayout(long long BH, long long S, long long D) {
+    flags_off = kHeader;
+    long long nq_max = (S + (long long)kMinBlockQ - 1) / (long long)kMinBlockQ;
+    flags_bytes = (size_t)(BH * nq_max) * kFlagStride;
+    delta_off = align(flags_off + flags_bytes);
+    delta_bytes = (size_t)(BH * S) * 4;
+    dqacc_off = align(delta_off + delta_bytes);
+    dqacc_bytes = (size_t)(BH * S * D) * 4;
+    total = align(dqacc_off + dqacc_bytes);
+  }
+  __host__ __device__ static size_t align(size_t x) { return (x + 255) & ~(size_t)255; }
+};
+
+enum DeviceError : uint32_t { kErrNone = 0, kErrTimeout = 1 };
+
+}  // namespace detattn

@@ -1,0 +1,126 @@
+// Attention forward for gfx950: produces O (bf16) and LSE (fp32, natural log),
+// the inputs of the backward. Deterministic by construction: each output row
+// is owned by one wave and reduced in a fixed order.
+//
+// A workgroup of 4 waves owns 128 query rows (32 per wave, kept in registers)
+// and streams KV tiles of 64 rows through LDS. Each wave computes the scores
+// transposed, S^T = K Q^T, so that in the MFMA accumulator layout every lane
+// owns one query (its column) and the running max / sum of the online softmax
+// are per-lane scalars; O^T = V^T P^T then takes P^T straight from the
+// accumulator registers, and the rescaling of O^T is per lane as well.
+#pragma once
+#include "common.h"
+
+namespace detattn {
+
+template <int D>
+struct FwdCfg {
+  static constexpr int BQ = 128;
+  static constexpr int BKV = 64;
+  static constexpr int KD = D / 16;
+  static constexpr int ND = D / 32;
+  static constexpr int MK = BKV / 32;   // 32-row KV blocks per tile
+  static constexpr int KK = BKV / 16;   // K steps over a KV tile
+  static constexpr int P = D + 8;       // LDS pitch
+  static constexpr int LDS_BYTES = 2 * BKV * P * 2;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                                     const __bf16* __restrict__ v, __bf16* __restrict__ o,
+                                                     float* __restrict__ lse, int S, float scale) {
+  using C = FwdCfg<D>;
+  __shared__ __attribute__((aligned(16))) __bf16 sK[C::BKV * C::P];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[C::BKV * C::P];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, c32 = lane & 31;
+  const int bh = blockIdx.y;
+  const int q0 = blockIdx.x * C::BQ + 32 * w;  // this wave's first query row
+  const long long head = (long long)bh * S * D;
+  const float c1 = scale * kLog2e;
+
+  // Q^T as B operand: lane holds Q[q0 + c32][16s + 8g .. +7]
+  bf16x8 qB[C::KD];
+#pragma unroll
+  for (int s = 0; s < C::KD; ++s)
+    qB[s] = *reinterpret_cast<const bf16x8*>(q + head + (long long)(q0 + c32) * D + 16 * s + 8 * g);
+
+  f32x16 oAcc[C::ND];
+#pragma unroll
+  for (int n = 0; n < C::ND; ++n) oAcc[n] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;  // log2 units; per lane = per query q0 + c32
+  const int qi = q0 + c32;
+
+  const int kv_end = CAUSAL ? (blockIdx.x + 1) * C::BQ : S;
+  for (int kv0 = 0; kv0 < kv_end; kv0 += C::BKV) {
+    __syncthreads();
+    constexpr int CPR = D / 8;
+    for (int cidx = tid; cidx < C::BKV * CPR; cidx += 256) {
+      const int r = cidx / CPR, x = cidx % CPR;
+      lds_store16(sK + r * C::P + 8 * x, *reinterpret_cast<const bf16x8*>(k + head + (long long)(kv0 + r) * D + 8 * x));
+      lds_store16(sV + r * C::P + 8 * x, *reinterpret_cast<const bf16x8*>(v + head + (long long)(kv0 + r) * D + 8 * x));
+    }
+    __syncthreads();
+    if (CAUSAL && kv0 > q0 + 31) continue;  // whole tile masked for this wave
+
+    // S^T = K Q^T : rows kv, columns q (lane)
+    f32x16 sAcc[C::MK];
+#pragma unroll
+    for (int mb = 0; mb < C::MK; ++mb) sAcc[mb] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < C::KD; ++s)
+#pragma unroll
+      for (int mb = 0; mb < C::MK; ++mb) sAcc[mb] = mfma32(frag_row(sK, C::P, 32 * mb, 16 * s), qB[s], sAcc[mb]);
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < C::MK; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = sAcc[mb][r] * c1;
+        const int kv = kv0 + 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (CAUSAL && kv > qi) x = -INFINITY;
+        sAcc[mb][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);  // finite: key 0 is visible to every query
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float lsum = 0.f;
+    bf16x8 pB[C::KK];
+#pragma unroll
+    for (int mb = 0; mb < C::MK; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(sAcc[mb][r] - m_new);
+        const __bf16 pb = (__bf16)p;
+        lsum += p;
+        pB[2 * mb + (r >> 3)][r & 7] = pb;
+      }
+    lsum += __shfl_xor(lsum, 32);
+    l_run = l_run * alpha + lsum;
+    m_run = m_new;
+#pragma unroll
+    for (int n = 0; n < C::ND; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oAcc[n][r] *= alpha;
+    // O^T += V^T P^T : A = V^T (rows d, K = kv in the accumulator permutation), B = P^T
+#pragma unroll
+    for (int s = 0; s < C::KK; ++s)
+#pragma unroll
+      for (int n = 0; n < C::ND; ++n) oAcc[n] = mfma32(frag_tr(sV, C::P, 16 * s, 32 * n, true), pB[s], oAcc[n]);
+  }
+
+  const float inv = 1.f / l_run;
+#pragma unroll
+  for (int n = 0; n < C::ND; ++n)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int d0 = 32 * n + 8 * rq + 4 * g;
+      bf16x4 v4 = to_bf16x4(oAcc[n][4 * rq] * inv, oAcc[n][4 * rq + 1] * inv, oAcc[n][4 * rq + 2] * inv,
+                            oAcc[n][4 * rq + 3] * inv);
+      *reinterpret_cast<bf16x4*>(o + head + (long long)qi * D + d0) = v4;
+    }
+  if (g == 0) lse[(long long)bh * S + qi] = (m_run + __log2f(l_run)) * 0.6931471805599453f;
+}
+
+}  // namespace detattn

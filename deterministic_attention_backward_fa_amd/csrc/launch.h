@@ -1,0 +1,36 @@
+// Internal interface between the C ABI (capi.cpp) and the kernel translation
+// units (one per head dimension, so their template instantiations compile in
+// parallel).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bwd_kernels.h"
+
+namespace detattn {
+
+struct MainLaunch {
+  BwdArgs args;
+  int D, BQ, BKV, causal, dq_mode;  // dq_mode: DqMode
+  int grid;
+  int cooperative;
+};
+
+// Kernel attributes for one main-kernel instantiation.
+struct MainInfo {
+  const void* func;  // kernel symbol, or nullptr if the combination is not built
+  int lds_bytes;
+  int occupancy;     // workgroups per compute unit (0 if unknown)
+};
+
+MainInfo main_info_d64(int BQ, int BKV, int causal, int dq_mode);
+MainInfo main_info_d128(int BQ, int BKV, int causal, int dq_mode);
+
+hipError_t launch_pre(int D, const __bf16* o, const __bf16* dout, float* delta, long long rows, int* flags,
+                      long long n_flags, unsigned* header, float* dqacc, long long dqacc_elems, hipStream_t st);
+hipError_t launch_convert(const float* acc, __bf16* dq, long long elems, float scale, hipStream_t st);
+hipError_t launch_main(const MainLaunch& L, hipStream_t st);
+hipError_t launch_fwd(int D, int causal, const __bf16* q, const __bf16* k, const __bf16* v, __bf16* o, float* lse,
+                      int BH, int S, float scale, hipStream_t st);
+
+}  // namespace detattn

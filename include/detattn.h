@@ -1,0 +1,185 @@
+/*
+ * detattn: deterministic FlashAttention-style attention backward for AMD
+ * MI355X (gfx950), with the DASH tile schedules.
+ *
+ * Operation (all entry points). Softmax attention over one sequence per
+ * (batch, head): O = softmax(scale * Q K^T [+ causal mask]) V. The backward
+ * produces dQ, dK, dV from Q, K, V, O, dO and the row log-sum-exp. The pages
+ * this library follows (DASH: Deterministic Attention Scheduling for
+ * High-throughput Reproducible LLM Training; zskr.cn explainer section 2.1 and
+ * gist.science summary section 1) describe the tiled backward in which every
+ * compute unit produces partial dQ/dK/dV and the dQ partials are reduced
+ * globally; a deterministic backward fixes the order of that reduction. The
+ * schedules below change only the order in which tiles are visited and dQ
+ * partials are added (sections 3.1-3.3 of the explainer; 2.2 of the summary).
+ *
+ * Conventions shared by every entry point:
+ *  - Tensors are contiguous [B, H, S, D], element (b, h, s, d) at
+ *    ((b*H + h)*S + s)*D + d. Q, K, V, O, dO, dQ, dK, dV are bf16 (uint16_t
+ *    storage, round-to-nearest-even on output). LSE is fp32 [B, H, S], natural
+ *    log of sum_j exp(scale * q_i . k_j) over the visible keys.
+ *  - Causal mask: key position j is visible from query position i iff j <= i
+ *    (one sequence length for queries and keys).
+ *  - All tensor and workspace pointers are DEVICE pointers, 16-byte aligned,
+ *    owned by the caller. The library never allocates or frees device memory
+ *    and keeps no device state between calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls are asynchronous: they enqueue kernels and return.
+ *  - Return value: a detattn_status_t. Argument errors return before anything
+ *    is enqueued. No C++ exception crosses this interface.
+ *  - Supported now: D in {64, 128}; S a multiple of 64 (and of the chosen KV
+ *    tile); B*H*S*D < 2^31. B*H == 0 or S == 0 is a valid empty call.
+ */
+#ifndef DETATTN_H_
+#define DETATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+  int32_t B, H, S, D;
+  float softmax_scale; /* usually 1/sqrt(D) */
+} detattn_shape_t;
+
+typedef enum { DETATTN_MASK_FULL = 0, DETATTN_MASK_CAUSAL = 1 } detattn_mask_t;
+
+/*
+ * Schedules (order of tile visits and of dQ accumulation):
+ *  SERIAL_ASCENDING  each KV tile walks its Q tiles upward; dQ tile i adds the
+ *                    KV tiles' partials in ascending order: the FA3
+ *                    deterministic baseline (explainer 2.1; summary 1).
+ *  DESCENDING_Q      Q tiles from the last down to the first; same dQ order as
+ *                    SERIAL_ASCENDING, so dQ is bit-identical to it
+ *                    (explainer 3.1; summary 2.2A).
+ *  SHIFT             full mask only: the workgroup holding KV tile j starts at
+ *                    Q tile j*r and wraps around; dQ order = step order
+ *                    (explainer 3.2; summary 2.2B).
+ *  SYMMETRIC_SHIFT   causal mask only, even number of KV tiles: KV tiles p and
+ *                    n-1-p share a workgroup; dense lower-left rectangle first,
+ *                    then the folded triangle (explainer 3.3; summary 2.2B).
+ *  ATOMIC_NONDET     unordered fp32 atomic adds of the dQ partials: the
+ *                    non-deterministic speed reference (explainer 2.1;
+ *                    summary 1). dK and dV remain deterministic.
+ */
+typedef enum {
+  DETATTN_SERIAL_ASCENDING = 0,
+  DETATTN_DESCENDING_Q = 1,
+  DETATTN_SHIFT = 2,
+  DETATTN_SYMMETRIC_SHIFT = 3,
+  DETATTN_ATOMIC_NONDET = 4
+} detattn_schedule_t;
+
+typedef enum {
+  DETATTN_OK = 0,
+  DETATTN_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad enum, negative size */
+  DETATTN_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement */
+  DETATTN_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+  DETATTN_ERR_HIP = 4,           /* a HIP runtime call failed (launch, copy, sync) */
+  DETATTN_ERR_DEVICE_TIMEOUT = 5 /* an ordered dQ wait timed out on the device */
+} detattn_status_t;
+
+/* dQ accumulation mechanism for the ordered schedules. */
+typedef enum {
+  DETATTN_DQ_DEFAULT = 0,
+  DETATTN_DQ_ORDERED_RMW = 1,   /* load + add + store of the fp32 accumulator, in rank order */
+  DETATTN_DQ_ORDERED_ATOMIC = 2 /* fp32 atomic adds issued in rank order (same order, same bits per run) */
+} detattn_dq_mode_t;
+
+/*
+ * Optional knobs of attn_bwd_deterministic_ex. Zero-initialise and set what you
+ * need; zero always means "library default".
+ */
+typedef struct {
+  int32_t block_q;           /* Q tile rows BQ: 0, 64 or 128 */
+  int32_t block_kv;          /* KV tile rows BKV: 0, 64 or 128 (BQ must divide BKV) */
+  int32_t grid;              /* persistent workgroups; 0 = one per compute unit x occupancy */
+  int32_t xcd_remap;         /* 0 = default (on), 1 = on, 2 = off: keep a ring of workgroups on one XCD */
+  int32_t dq_mode;           /* detattn_dq_mode_t */
+  uint32_t debug_delay_seed; /* testing: != 0 injects pseudo-random delays before each ordered dQ add */
+  uint32_t timeout_us;       /* bound on one ordered wait; 0 = default (4 s) */
+  int32_t debug_skip_signal; /* testing: > 0 makes the workgroup of item (debug_skip_signal - 1) never
+                                signal its first dQ tile, so its successor times out (forces the
+                                failure path; every kernel still exits) */
+  void* main_begin_event;    /* optional hipEvent_t recorded on `stream` right before the main kernel */
+  void* main_end_event;      /* optional hipEvent_t recorded on `stream` right after the main kernel */
+} detattn_bwd_options_t;
+
+/* What the library chose for a call (see detattn_bwd_plan). */
+typedef struct {
+  int32_t block_q, block_kv, n_q, n_kv;
+  int32_t items;       /* items over all heads */
+  int32_t grid;        /* workgroups launched */
+  int32_t ring;        /* workgroups per co-resident ring (shift schedules), else 0 */
+  int32_t rings;       /* rings running at once, else 0 */
+  int32_t dq_mode;     /* resolved detattn_dq_mode_t (0 for ATOMIC_NONDET) */
+  int32_t cooperative; /* 1 if launched as a cooperative (co-resident) grid */
+} detattn_plan_t;
+
+/*
+ * Forward that produces the backward's inputs O and LSE. Not part of the
+ * timed backward; deterministic (no cross-workgroup reduction).
+ * q, k, v: bf16 [B,H,S,D] in; o: bf16 [B,H,S,D] out; lse: fp32 [B,H,S] out.
+ * Requires S % 128 == 0 for now.
+ */
+int detattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, detattn_shape_t shape,
+                detattn_mask_t mask, void* stream);
+
+/* Bytes of device workspace attn_bwd_deterministic needs for `shape`
+ * (independent of mask, schedule and options). 0 on invalid shapes. */
+size_t detattn_bwd_workspace_bytes(detattn_shape_t shape, detattn_mask_t mask, detattn_schedule_t schedule);
+
+/*
+ * Deterministic attention backward (preprocess D = rowsum(dO * O), main kernel,
+ * dQ fp32 -> bf16 convert), enqueued on `stream`.
+ *  q, k, v, o, dout : bf16 [B,H,S,D] in
+ *  lse              : fp32 [B,H,S] in (natural log, as detattn_fwd writes it)
+ *  dq, dk, dv       : bf16 [B,H,S,D] out (may not alias inputs)
+ *  workspace        : >= detattn_bwd_workspace_bytes(...) bytes, 256-byte aligned;
+ *                     overwritten; one workspace per concurrently running call
+ * Results are bit-identical across runs for every schedule except
+ * ATOMIC_NONDET's dQ; SERIAL_ASCENDING and DESCENDING_Q give identical dQ.
+ * Device-side wait timeouts are reported by detattn_device_status.
+ */
+int attn_bwd_deterministic(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                           detattn_shape_t shape, detattn_mask_t mask, detattn_schedule_t schedule, void* stream);
+
+/* Same as attn_bwd_deterministic with explicit options (NULL = defaults). */
+int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                              const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                              size_t workspace_bytes, detattn_shape_t shape, detattn_mask_t mask,
+                              detattn_schedule_t schedule, const detattn_bwd_options_t* options, void* stream);
+
+/* Resolve tiles, grid and rings for a call without launching anything.
+ * Needs a HIP device for the compute-unit count unless options->grid > 0. */
+int detattn_bwd_plan(detattn_shape_t shape, detattn_mask_t mask, detattn_schedule_t schedule,
+                     const detattn_bwd_options_t* options, detattn_plan_t* plan);
+
+/* Synchronise `stream` and read the device error word of the last call that
+ * used `workspace`: DETATTN_OK or DETATTN_ERR_DEVICE_TIMEOUT (or ERR_HIP). */
+int detattn_device_status(void* workspace, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* detattn_status_string(int status);
+
+/*
+ * Host-side view of a schedule, the same integer functions the device uses.
+ * For item `item` (a KV tile, or a symmetric pair index) of one head with
+ * n_q Q tiles and n_kv KV tiles: writes up to `cap` entries of its visit
+ * sequence (Q tile, KV tile, rank of that KV tile in the dQ tile's order) and
+ * returns the item's length, or -1 on invalid arguments.
+ */
+int detattn_schedule_item(int32_t schedule, int32_t mask, int32_t n_q, int32_t n_kv, int32_t item,
+                          int32_t* q_tiles, int32_t* kv_tiles, int32_t* ranks, int32_t cap);
+
+/* Items per head of a schedule (n_kv, or n_kv/2 for SYMMETRIC_SHIFT); -1 if invalid. */
+int detattn_schedule_items_per_head(int32_t schedule, int32_t mask, int32_t n_q, int32_t n_kv);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DETATTN_H_ */

@@ -1,0 +1,157 @@
+"""Host-side checks of libdetattn that need no GPU.
+
+Every call here returns before anything is enqueued (argument, support and
+workspace errors, planning with an explicit grid, the schedule view), so the
+file is safe on a machine with or without a GPU; no test passes a fake
+pointer to a call that could launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import deterministic_attention_backward_fa_amd as da
+from oracle import schedules as OS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "detattn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    names = declared_functions()
+    assert "attn_bwd_deterministic" in names and "detattn_fwd" in names and len(names) >= 9
+    L = ctypes.CDLL(da.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in include/detattn.h but not exported"
+
+
+def test_status_strings():
+    for code in range(6):
+        assert da.status_string(code) and da.status_string(code) != "unknown status"
+    assert da.status_string(99) == "unknown status"
+
+
+def test_workspace_bytes():
+    B, H, S, D = 1, 32, 8192, 128
+    n = da.detattn_bwd_workspace_bytes(B, H, S, D)
+    # fp32 dQ accumulator + fp32 D + one 128-byte flag line per 64-row Q tile + header, 256-byte aligned
+    assert n >= 4 * B * H * S * D + 4 * B * H * S + 128 * B * H * (S // 64) + 256
+    assert n % 256 == 0
+    assert da.detattn_bwd_workspace_bytes(1, 1, 64, -1) == 0
+
+
+def _bwd_status(shape, mask=0, sched=0, ptr=0x10000, ws=0x20000, ws_bytes=1 << 40, opts=None):
+    L = da.lib()
+    p = ctypes.c_void_p(ptr)
+    args = [p] * 9 + [ctypes.c_void_p(ws), ctypes.c_size_t(ws_bytes), da.Shape(*shape), mask, sched]
+    if opts is None:
+        return L.attn_bwd_deterministic(*args, None)
+    return L.attn_bwd_deterministic_ex(*args, ctypes.byref(opts), None)
+
+
+def test_argument_errors_return_before_launch():
+    # null pointers
+    assert _bwd_status((1, 1, 128, 64, 0.125), ptr=0) == 1
+    # misaligned pointer
+    assert _bwd_status((1, 1, 128, 64, 0.125), ptr=0x10008) == 1
+    # bad enums
+    assert _bwd_status((1, 1, 128, 64, 0.125), mask=7) == 1
+    assert _bwd_status((1, 1, 128, 64, 0.125), sched=9) == 1
+    # negative size
+    assert _bwd_status((1, -1, 128, 64, 0.125)) == 1
+    # empty problems are a valid no-op
+    assert _bwd_status((0, 4, 128, 64, 0.125)) == 0
+    assert _bwd_status((2, 4, 0, 64, 0.125)) == 0
+
+
+def test_unsupported_configurations():
+    # head dimension not built
+    assert _bwd_status((1, 1, 128, 96, 0.1)) == 2
+    # S not a multiple of the tile
+    assert _bwd_status((1, 1, 100, 64, 0.125), opts=da._options(grid=8)) == 2
+    # shift is defined for full masks only, symmetric shift for causal masks only
+    assert _bwd_status((1, 1, 256, 64, 0.125), mask=1, sched=2, opts=da._options(grid=8)) == 2
+    assert _bwd_status((1, 1, 256, 64, 0.125), mask=0, sched=3, opts=da._options(grid=8)) == 2
+    # symmetric shift needs an even number of KV tiles (3 tiles of 64 rows)
+    assert _bwd_status((1, 1, 192, 64, 0.125), mask=1, sched=3, opts=da._options(grid=8, block_q=64,
+                                                                                     block_kv=64)) == 2
+    # a tile pair that is not built
+    assert _bwd_status((1, 1, 256, 128, 0.1), opts=da._options(grid=8, block_q=128, block_kv=128)) == 2
+    # a ring larger than the grid cannot be co-resident
+    assert _bwd_status((1, 1, 1024, 64, 0.125), sched=2, opts=da._options(grid=8, block_q=64, block_kv=64)) == 2
+
+
+def test_workspace_errors():
+    o = da._options(grid=8)
+    assert _bwd_status((1, 1, 128, 64, 0.125), ws=0, opts=o) == 3
+    assert _bwd_status((1, 1, 128, 64, 0.125), ws=0x20010, opts=o) == 3  # not 256-byte aligned
+    need = da.detattn_bwd_workspace_bytes(1, 1, 128, 64)
+    assert _bwd_status((1, 1, 128, 64, 0.125), ws_bytes=need - 1, opts=o) == 3
+
+
+def test_fwd_argument_errors():
+    L = da.lib()
+    p = ctypes.c_void_p(0x10000)
+    assert L.detattn_fwd(p, p, p, p, ctypes.c_void_p(0), da.Shape(1, 1, 128, 64, 0.1), 0, None) == 1
+    assert L.detattn_fwd(p, p, p, p, p, da.Shape(1, 1, 128, 80, 0.1), 0, None) == 2
+    assert L.detattn_fwd(p, p, p, p, p, da.Shape(1, 1, 96, 64, 0.1), 0, None) == 2
+    assert L.detattn_fwd(p, p, p, p, p, da.Shape(1, 1, 128, 64, 0.1), 5, None) == 1
+    assert L.detattn_fwd(p, p, p, p, p, da.Shape(0, 1, 128, 64, 0.1), 0, None) == 0
+
+
+@pytest.mark.parametrize("cfg", [
+    # (B, H, S, D, causal, schedule, expected block_q, block_kv)
+    (1, 2, 256, 64, False, "shift", 64, 64),
+    (4, 16, 2048, 64, True, "symmetric_shift", 128, 128),
+    (2, 32, 4096, 128, False, "shift", 64, 128),
+    (1, 32, 8192, 128, True, "symmetric_shift", 64, 128),
+    (1, 16, 16384, 128, False, "shift", 64, 64),
+    (1, 16, 16384, 128, True, "symmetric_shift", 64, 64),
+])
+def test_default_tiles_and_rings(cfg):
+    B, H, S, D, causal, sched, bq, bkv = cfg
+    p = da.detattn_bwd_plan(B, H, S, D, causal, sched, grid=256)
+    assert (p["block_q"], p["block_kv"]) == (bq, bkv)
+    n_kv = S // bkv
+    ring = n_kv if sched == "shift" else n_kv // 2
+    assert p["ring"] == ring and p["cooperative"] == 1
+    assert p["grid"] == p["rings"] * ring <= 256
+    assert p["rings"] >= 1
+
+
+def test_ticket_plan_caps_grid_at_items():
+    p = da.detattn_bwd_plan(1, 2, 256, 64, False, "serial_ascending", grid=256)
+    assert p["items"] == 2 * 4 and p["grid"] == 8 and p["ring"] == 0 and p["cooperative"] == 0
+
+
+CASES = [(n_kv, r) for n_kv in (1, 2, 4, 6, 8, 16, 32) for r in (1, 2)]
+
+
+@pytest.mark.parametrize("n_kv,r", CASES)
+@pytest.mark.parametrize("sched,mask", [("serial_ascending", "full"), ("serial_ascending", "causal"),
+                                        ("descending_q", "full"), ("descending_q", "causal"),
+                                        ("shift", "full"), ("symmetric_shift", "causal"),
+                                        ("atomic_nondet", "full"), ("atomic_nondet", "causal")])
+def test_library_schedule_matches_oracle(sched, mask, n_kv, r):
+    """The library's closed-form visit orders and ranks equal the oracle's
+    definitions (built by sorting contributions by step)."""
+    n_q = n_kv * r
+    causal = mask == "causal"
+    if not OS.valid(sched, mask, n_q, n_kv):
+        assert da.detattn_schedule_items_per_head(sched, causal, n_q, n_kv) == -1
+        return
+    want_items = OS.items(sched, mask, n_q, n_kv)
+    assert da.detattn_schedule_items_per_head(sched, causal, n_q, n_kv) == len(want_items)
+    ranks = OS.rank_table(sched, mask, n_q, n_kv) if sched != "atomic_nondet" else None
+    for it, want in enumerate(want_items):
+        got = da.detattn_schedule_item(sched, causal, n_q, n_kv, it)
+        assert [(a, b) for a, b, _ in got] == want
+        if ranks is not None:
+            assert [c for _, _, c in got] == [ranks[t] for t in want]
