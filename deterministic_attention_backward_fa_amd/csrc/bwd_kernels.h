@@ -340,6 +340,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
             atomicAdd(dqt + (long long)qloc * D, dqAcc[m][r]);
           }
       } else {
+        // Ordered hand-off. The accumulator is only touched through agent-scope
+        // (coherent across XCDs) relaxed atomic accesses: sc1 loads/stores or fp32
+        // atomic adds. Ordering: the predecessor waits until its own accesses have
+        // completed (vmcnt 0 in every wave), then publishes rank+1 on the flag; the
+        // successor sees the flag through an sc1 load before issuing its accesses.
+        // No L2-wide writeback or invalidate is needed because no plain (possibly
+        // cached, non-coherent) access to the accumulator is ever made.
         const int rk = sc.rank(i, j);
         int* flag = a.flags + ((long long)bh * sc.n_q + i) * kFlagInts;
         if (tid == 0) {
@@ -360,30 +367,52 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
                 }
               }
             }
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
           }
         }
         __syncthreads();
-        if (rk > 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        if (rk == 0) {
 #pragma unroll
-        for (int m = 0; m < C::MQD; ++m)
+          for (int m = 0; m < C::MQD; ++m)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qloc = 32 * (mq0 + m) + 8 * (r >> 2) + 4 * g + (r & 3);
-            float* p = dqt + (long long)qloc * D;
-            if (rk == 0) {
-              *p = dqAcc[m][r];
-            } else if constexpr (DQM == kDqOrderedAtomic) {
-              __hip_atomic_fetch_add(p, dqAcc[m][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            } else {
-              *p = *p + dqAcc[m][r];
+            for (int r = 0; r < 16; ++r) {
+              const int qloc = 32 * (mq0 + m) + 8 * (r >> 2) + 4 * g + (r & 3);
+              __hip_atomic_store(dqt + (long long)qloc * D, dqAcc[m][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-          }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        } else if constexpr (DQM == kDqOrderedAtomic) {
+#pragma unroll
+          for (int m = 0; m < C::MQD; ++m)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int qloc = 32 * (mq0 + m) + 8 * (r >> 2) + 4 * g + (r & 3);
+              __hip_atomic_fetch_add(dqt + (long long)qloc * D, dqAcc[m][r], __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+            }
+        } else {
+          float old[C::MQD][16];
+#pragma unroll
+          for (int m = 0; m < C::MQD; ++m)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int qloc = 32 * (mq0 + m) + 8 * (r >> 2) + 4 * g + (r & 3);
+              old[m][r] = __hip_atomic_load(dqt + (long long)qloc * D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+          for (int m = 0; m < C::MQD; ++m)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int qloc = 32 * (mq0 + m) + 8 * (r >> 2) + 4 * g + (r & 3);
+              __hip_atomic_store(dqt + (long long)qloc * D, old[m][r] + dqAcc[m][r], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        // every wave: its accumulator accesses are complete before the barrier
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __syncthreads();
         if (tid == 0) {
           const bool withhold = (a.skip_item >= 0 && gidx == a.skip_item && t == 0);
-          if (!withhold) __hip_atomic_store(flag, rk + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+          if (!withhold) __hip_atomic_store(flag, rk + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
 
