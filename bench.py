@@ -72,13 +72,13 @@ def tiles_executed(plan, B, H, causal):
     return B * H * per_head
 
 
-def time_schedule(da, torch, ev, tensors, shape, causal, sched, steps, warmup):
+def time_schedule(da, torch, ev, tensors, shape, causal, sched, steps, warmup, **opts):
     q, k, v, o, do, lse = tensors
     B, H, S, D = shape
     ws = da.alloc_workspace(B, H, S, D)
     out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     for _ in range(warmup):
-        da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule=sched, workspace=ws, out=out)
+        da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule=sched, workspace=ws, out=out, **opts)
     torch.cuda.synchronize()
     ref = [t.clone() for t in out]
     begins = [ev.create() for _ in range(steps)]
@@ -89,7 +89,7 @@ def time_schedule(da, torch, ev, tensors, shape, causal, sched, steps, warmup):
     t0.record()
     for s in range(steps):
         da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule=sched, workspace=ws, out=out,
-                                  main_begin_event=begins[s], main_end_event=ends[s])
+                                  main_begin_event=begins[s], main_end_event=ends[s], **opts)
     t1.record()
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
@@ -137,6 +137,10 @@ def main():
     ap.add_argument("--schedule", default=None, help="headline schedule (default: shift / symmetric_shift)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-headline", action="store_true", help="skip the other schedules")
+    ap.add_argument("--dq-mode", default="default", choices=["default", "rmw", "atomic"],
+                    help="ordered dQ accumulation mechanism for the deterministic schedules")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path",
@@ -144,6 +148,15 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copied 3 x 1 GiB")
+        return
 
     import deterministic_attention_backward_fa_amd as da
     from deterministic_attention_backward_fa_amd.synth import make_qkvdo
@@ -164,7 +177,8 @@ def main():
     results = {}
     for sched in scheds:
         log(f"[bench] timing {sched}: warmup {args.warmup}, steps {args.steps}")
-        r = time_schedule(da, torch, ev, tensors, (B, H, S, D), causal, sched, args.steps, args.warmup)
+        opts = {"dq_mode": args.dq_mode} if (args.dq_mode != "default" and sched != "atomic_nondet") else {}
+        r = time_schedule(da, torch, ev, tensors, (B, H, S, D), causal, sched, args.steps, args.warmup, **opts)
         r["tflops"] = flops / (r["ms_per_step"] * 1e-3) / 1e12
         results[sched] = r
         log(f"[bench] {sched}: {r['ms_per_step']:.3f} ms/step, main {r['main_ms']:.3f} ms, "

@@ -10,7 +10,7 @@ MainInfo info_of() {
     MainInfo m;
     auto fn = &bwd_main_kernel<D, BQ, BKV, CAUSAL, DQM>;
     m.func = reinterpret_cast<const void*>(fn);
-    m.lds_bytes = BwdCfg<D, BQ, BKV>::LDS_BYTES;
+    m.lds_bytes = MainCfg<D, BQ, BKV>::LDS_BYTES;
     int occ = 0;
     if (hipFuncSetAttribute(m.func, hipFuncAttributeMaxDynamicSharedMemorySize, m.lds_bytes) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kThreads, m.lds_bytes) != hipSuccess)

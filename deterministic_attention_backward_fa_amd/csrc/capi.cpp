@@ -91,7 +91,7 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
   int dqm = kDqUnordered;
   int pub_dqm = 0;
   if (sch != DETATTN_ATOMIC_NONDET) {
-    pub_dqm = o.dq_mode ? o.dq_mode : DETATTN_DQ_ORDERED_RMW;
+    pub_dqm = o.dq_mode ? o.dq_mode : DETATTN_DQ_ORDERED_ATOMIC;
     dqm = pub_dqm == DETATTN_DQ_ORDERED_ATOMIC ? kDqOrderedAtomic : kDqOrderedRmw;
   }
   const MainInfo info = s.D == 64 ? main_info_d64(bq, bkv, causal, dqm) : main_info_d128(bq, bkv, causal, dqm);

@@ -110,6 +110,88 @@ __device__ __forceinline__ bf16x8 frag_row(const __bf16* M, int pitch, int r0, i
   return lds_load16(M + (r0 + (l & 31)) * pitch + k0 + 8 * (l >> 5));
 }
 
+// ---------------------------------------------------------------------------
+// Swizzled LDS tiles. A tile of R rows x (NCH 16-byte chunks) is stored without
+// padding; logical chunk c of row r sits at physical chunk c ^ swz_f<NCH>(r).
+// The XOR pattern makes both access patterns used on these tiles hit distinct
+// LDS banks (64 banks x 4 bytes): 16 consecutive rows read at one chunk
+// (16-byte row fragments), and 4 consecutive rows x 4 consecutive chunks
+// (transpose reads of two 16-lane groups).
+// ---------------------------------------------------------------------------
+template <int NCH>
+__device__ __forceinline__ int swz_f(int r) {
+  static_assert(NCH == 8 || NCH == 16, "rows of 128 or 256 bytes");
+  if constexpr (NCH == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Element offset of (row r, column c) in a swizzled bf16 tile.
+template <int NCH>
+__device__ __forceinline__ int swz_off(int r, int c) {
+  return r * (NCH * 8) + ((((c >> 3) ^ swz_f<NCH>(r))) << 3) + (c & 7);
+}
+
+// frag_row on a swizzled tile: lane holds M[r0 + l%32][k0 + 8g .. +7].
+template <int NCH>
+__device__ __forceinline__ bf16x8 frag_row_s(const __bf16* M, int r0, int k0) {
+  const int l = threadIdx.x & 63;
+  return lds_load16(M + swz_off<NCH>(r0 + (l & 31), k0 + 8 * (l >> 5)));
+}
+
+// frag_tr on a swizzled tile (same meaning as frag_tr).
+template <int NCH>
+__device__ __forceinline__ bf16x8 frag_tr_s(const __bf16* M, int k0, int c0, bool perm) {
+  const int l = threadIdx.x & 63;
+  const int s = l & 15;
+  const int grp = l >> 4;
+  const int g = grp >> 1;
+  const int cbase = c0 + 16 * (grp & 1) + 4 * (s & 3);
+  int ka, kb;
+  if (perm) {
+    ka = k0 + 4 * g + (s >> 2);
+    kb = ka + 8;
+  } else {
+    ka = k0 + 8 * g + (s >> 2);
+    kb = ka + 4;
+  }
+  return cat(lds_read_tr(M + swz_off<NCH>(ka, cbase)), lds_read_tr(M + swz_off<NCH>(kb, cbase)));
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
+
+// Asynchronous global -> LDS copy of `rows` rows of NCH*8 bf16 (row-major,
+// contiguous in global memory) into a swizzled LDS tile, split over the 4
+// waves of the workgroup. Each wave instruction moves 1 KB: lane l writes the
+// 16 bytes at LDS offset 16*l of the instruction's block, so the swizzle is
+// applied by choosing which global chunk each lane fetches. Completion is
+// tracked by vmcnt.
+template <int NCH>
+__device__ __forceinline__ void dma_tile(__bf16* lds_tile, const __bf16* __restrict__ gsrc, int rows) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n_ins = rows * NCH / 64;
+  for (int ins = w; ins < n_ins; ins += 4) {
+    const int q = ins * 64 + lane;  // physical chunk index inside the tile
+    const int r = q / NCH, p = q % NCH;
+    const __bf16* src = gsrc + r * (NCH * 8) + ((p ^ swz_f<NCH>(r)) << 3);
+    __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)(lds_tile + ins * 512), 16, 0, 0);
+  }
+}
+
+// Asynchronous copy of n (a multiple of 64) fp32 values to LDS, by wave `wv`.
+__device__ __forceinline__ void dma_f32(float* lds, const float* __restrict__ gsrc, int n, int wv) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (w != wv) return;
+  for (int x = 0; x < n; x += 64)
+    __builtin_amdgcn_global_load_lds((gbl_void*)(gsrc + x + lane), (lds_void*)(lds + x), 4, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vm_all() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Workspace layout (all offsets in bytes from the workspace base).
 struct WsLayout {
   static constexpr size_t kHeader = 256;         // ticket @0, error word @64, error detail @128
