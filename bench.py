@@ -137,7 +137,7 @@ def main():
     ap.add_argument("--schedule", default=None, help="headline schedule (default: shift / symmetric_shift)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-headline", action="store_true", help="skip the other schedules")
-    ap.add_argument("--dq-mode", default="default", choices=["default", "rmw", "atomic"],
+    ap.add_argument("--dq-mode", default="default", choices=["default", "rmw", "atomic", "xcd_local"],
                     help="ordered dQ accumulation mechanism for the deterministic schedules")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")

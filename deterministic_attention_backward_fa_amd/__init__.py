@@ -15,9 +15,9 @@ LIB_PATH = os.path.join(_HERE, "libdetattn.so")
 
 MASKS = {"full": 0, "causal": 1}
 SCHEDULES = {"serial_ascending": 0, "descending_q": 1, "shift": 2, "symmetric_shift": 3, "atomic_nondet": 4}
-DQ_MODES = {"default": 0, "rmw": 1, "atomic": 2}
+DQ_MODES = {"default": 0, "rmw": 1, "atomic": 2, "xcd_local": 3}
 STATUS = {0: "OK", 1: "ERR_INVALID_ARG", 2: "ERR_UNSUPPORTED", 3: "ERR_WORKSPACE", 4: "ERR_HIP",
-          5: "ERR_DEVICE_TIMEOUT"}
+          5: "ERR_DEVICE_TIMEOUT", 6: "ERR_DEVICE_PLACEMENT"}
 
 
 class DetAttnError(RuntimeError):

@@ -28,10 +28,12 @@ MainInfo pick(int causal, int dqm) {
     if (dqm == kDqOrderedRmw) return info_of<128, BQ, BKV, true, kDqOrderedRmw>();
     if (dqm == kDqOrderedAtomic) return info_of<128, BQ, BKV, true, kDqOrderedAtomic>();
     if (dqm == kDqUnordered) return info_of<128, BQ, BKV, true, kDqUnordered>();
+    if (dqm == kDqLocalRmw) return info_of<128, BQ, BKV, true, kDqLocalRmw>();
   } else {
     if (dqm == kDqOrderedRmw) return info_of<128, BQ, BKV, false, kDqOrderedRmw>();
     if (dqm == kDqOrderedAtomic) return info_of<128, BQ, BKV, false, kDqOrderedAtomic>();
     if (dqm == kDqUnordered) return info_of<128, BQ, BKV, false, kDqUnordered>();
+    if (dqm == kDqLocalRmw) return info_of<128, BQ, BKV, false, kDqLocalRmw>();
   }
   return MainInfo{nullptr, 0, 0};
 }

@@ -33,6 +33,8 @@
 #include "common.h"
 #include "tile_sched.h"
 
+#include <type_traits>
+
 namespace detattn {
 
 template <int D, int BQ, int BKV>
@@ -123,6 +125,12 @@ __device__ __forceinline__ void store_column(f32x16 (&acc)[C::ND], float mul, __
 template <int D, int BQ, int BKV, bool CAUSAL, int DQM>
 __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   using C = MainCfg<D, BQ, BKV>;
+  // Scope of the accumulator accesses: across XCDs (sc1), or inside the XCD's
+  // L2 (sc0) when every workgroup of a ring runs on one XCD. sc0 loads may hit
+  // the compute unit's own L1, so that mode invalidates L1 (buffer_inv sc0)
+  // after observing the flag and before loading. Flags always use sc1.
+  constexpr int kScope = DQM == kDqLocalRmw ? __HIP_MEMORY_SCOPE_WORKGROUP : __HIP_MEMORY_SCOPE_AGENT;
+  constexpr int kFlagScope = __HIP_MEMORY_SCOPE_AGENT;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   __bf16* sK = reinterpret_cast<__bf16*>(smem + C::OFF_K);
   __bf16* sV = reinterpret_cast<__bf16*>(smem + C::OFF_V);
@@ -155,6 +163,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       slot = wg % a.ring;
     }
     if (ring_id >= a.rings) return;
+    if constexpr (DQM == kDqLocalRmw) {
+      // the ring placement assumes workgroup w runs on XCD w % 8: verify it
+      unsigned xcc;
+      asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+      if (tid == 0 && (int)(xcc & 0xF) != (wg & 7))
+        __hip_atomic_fetch_or(a.err, (unsigned)kErrPlacement, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 
   // Q, dO, LSE and D of Q tile i -> buffer b (asynchronous).
@@ -165,7 +180,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     float* ld = reinterpret_cast<float*>(smem + (b ? C::OFF_LD1 : C::OFF_LD0));
     dma_tile<C::NCH_D>(dq_, a.q + head_off + qrow0 * D, BQ);
     dma_tile<C::NCH_D>(ddo, a.dout + head_off + qrow0 * D, BQ);
-    dma_f32(ld, a.lse + bhS + qrow0, BQ, 0);
+    dma_f32(ld, a.lse2 + bhS + qrow0, BQ, 0);
     dma_f32(ld + BQ, a.delta + bhS + qrow0, BQ, 1);
   };
 
@@ -188,49 +203,43 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     const long long head_off = (long long)bh * a.S * D;
     const long long bhS = (long long)bh * a.S;
 
-    int cur_j = -1;
     int* pend_flag = nullptr;  // flag of the previous tile, published once its adds are complete
     int pend_val = 0;
-    bf16x8 kB[C::KD], vB[C::KD];
-    f32x16 dKacc[C::ND], dVacc[C::ND];
 
-    for (int t = 0; t < len; ++t) {
-      int i, j;
-      sc.tile(it, t, i, j);
-      const int b = t & 1;
+    for (int seg = 0; seg < sc.segments(); ++seg) {
+    const int t_begin = sc.seg_begin(it, seg), t_end = sc.seg_end(it, seg);
+    int i0, j;
+    sc.tile(it, t_begin, i0, j);
+    // ---- segment prologue: K_j, V_j and the first Q tile, synchronously ----
+    dma_tile<C::NCH_D>(sK, a.k + head_off + (long long)j * BKV * D, BKV);
+    dma_tile<C::NCH_D>(sV, a.v + head_off + (long long)j * BKV * D, BKV);
+    dma_q(0, head_off, bhS, i0);
+    wait_vm_all();
+    __syncthreads();
+    bf16x8 kB[C::KD], vB[C::KD];
+#pragma unroll
+    for (int s = 0; s < C::KD; ++s) {
+      kB[s] = frag_row_s<C::NCH_D>(sK, 32 * wk, 16 * s);
+      vB[s] = frag_row_s<C::NCH_D>(sV, 32 * wk, 16 * s);
+    }
+    f32x16 dKacc[C::ND], dVacc[C::ND];
+#pragma unroll
+    for (int n = 0; n < C::ND; ++n) {
+      dKacc[n] = f32x16{};
+      dVacc[n] = f32x16{};
+    }
+
+    int t = t_begin;
+    do {
+      int i, jj;
+      sc.tile(it, t, i, jj);
+      const int b = (t - t_begin) & 1;
       const long long qrow0 = (long long)i * BQ;
-      if (j != cur_j) {
-        // column start: K_j, V_j and this tile's inputs, synchronously
-        cur_j = j;
-        dma_tile<C::NCH_D>(sK, a.k + head_off + (long long)j * BKV * D, BKV);
-        dma_tile<C::NCH_D>(sV, a.v + head_off + (long long)j * BKV * D, BKV);
-        dma_q(b, head_off, bhS, i);
-        wait_vm_all();
-        __syncthreads();
-#pragma unroll
-        for (int s = 0; s < C::KD; ++s) {
-          kB[s] = frag_row_s<C::NCH_D>(sK, 32 * wk, 16 * s);
-          vB[s] = frag_row_s<C::NCH_D>(sV, 32 * wk, 16 * s);
-        }
-#pragma unroll
-        for (int n = 0; n < C::ND; ++n) {
-          dKacc[n] = f32x16{};
-          dVacc[n] = f32x16{};
-        }
-      } else {
-        // this tile's DMA (issued during the previous tile) and the previous
-        // tile's accumulator adds are complete in every wave
-        wait_vm_all();
-        __syncthreads();
-        if (tid == 0 && pend_flag)
-          __hip_atomic_store(pend_flag, pend_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        pend_flag = nullptr;
-      }
       // prefetch the next tile of this column into the other buffer
-      if (t + 1 < len) {
+      if (t + 1 < t_end) {
         int ni, nj;
         sc.tile(it, t + 1, ni, nj);
-        if (nj == j) dma_q(b ^ 1, head_off, bhS, ni);
+        dma_q(b ^ 1, head_off, bhS, ni);
       }
       const __bf16* sQ = reinterpret_cast<const __bf16*>(smem + (b ? C::OFF_Q1 : C::OFF_Q0));
       const __bf16* sdO = reinterpret_cast<const __bf16*>(smem + (b ? C::OFF_DO1 : C::OFF_DO0));
@@ -256,29 +265,45 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       }
 
       // ---- P and dS (C layout: row q, column kv = lane) ----
+      // Only tiles that straddle the diagonal need the causal mask.
       const bool diag = CAUSAL && ((long long)(j + 1) * BKV - 1 > qrow0);
-      const int kv_glob = j * BKV + 32 * wk + c32;
       bf16x8 pB[C::KQ], dsB[C::KQ];
+      auto elementwise = [&](auto masked) {
+        const int kv_rel = (int)((long long)j * BKV - qrow0) + 32 * wk + c32;  // kv - first q of the tile
 #pragma unroll
-      for (int mb = 0; mb < C::MQ; ++mb) {
+        for (int mb = 0; mb < C::MQ; ++mb) {
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int qloc = C::QW * wq + 32 * mb + 8 * rq + 4 * g;
-          const f32x4 L4 = *reinterpret_cast<const f32x4*>(sL + qloc);
-          const f32x4 D4 = *reinterpret_cast<const f32x4*>(sDl + qloc);
+          for (int rq = 0; rq < 4; ++rq) {
+            const int qloc = C::QW * wq + 32 * mb + 8 * rq + 4 * g;
+            const f32x4 L4 = *reinterpret_cast<const f32x4*>(sL + qloc);
+            const f32x4 D4 = *reinterpret_cast<const f32x4*>(sDl + qloc);
+            float p[4], ds[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * rq + e;
-            float p = __builtin_amdgcn_exp2f(sAcc[mb][r] * c1 - L4[e] * kLog2e);
-            if (diag && kv_glob > (int)qrow0 + qloc + e) p = 0.f;
-            const float ds = p * (pAcc[mb][r] - D4[e]);
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * rq + e;
+              p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sAcc[mb][r], c1, -L4[e]));
+              if constexpr (decltype(masked)::value) {
+                if (kv_rel > qloc + e) p[e] = 0.f;
+              }
+              ds[e] = p[e] * (pAcc[mb][r] - D4[e]);
+            }
             const int kstep = 2 * mb + (rq >> 1);
-            const int slotx = 4 * (rq & 1) + e;
-            pB[kstep][slotx] = (__bf16)p;
-            dsB[kstep][slotx] = (__bf16)ds;
+            const int sl = 4 * (rq & 1);
+            const bf16x2 p01 = cvt2(p[0], p[1]), p23 = cvt2(p[2], p[3]);
+            const bf16x2 d01 = cvt2(ds[0], ds[1]), d23 = cvt2(ds[2], ds[3]);
+            pB[kstep][sl] = p01[0];
+            pB[kstep][sl + 1] = p01[1];
+            pB[kstep][sl + 2] = p23[0];
+            pB[kstep][sl + 3] = p23[1];
+            dsB[kstep][sl] = d01[0];
+            dsB[kstep][sl + 1] = d01[1];
+            dsB[kstep][sl + 2] = d23[0];
+            dsB[kstep][sl + 3] = d23[1];
           }
         }
-      }
+      };
+      if (diag) elementwise(std::true_type{});
+      else elementwise(std::false_type{});
 
       // ---- dS^T -> LDS (row kv, column q), 4 consecutive q per 8-byte store ----
 #pragma unroll
@@ -328,12 +353,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
           if (rk > 0) {
             const long long t0 = now_ticks();
             int spins = 0;
-            while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != rk) {
+            while (__hip_atomic_load(flag, __ATOMIC_RELAXED, kFlagScope) != rk) {
               __builtin_amdgcn_s_sleep(1);
               if (((++spins) & 255) == 0) {
                 if (now_ticks() - t0 > a.timeout_ticks ||
                     __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
-                  __hip_atomic_store(a.err, (unsigned)kErrTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                  __hip_atomic_fetch_or(a.err, (unsigned)kErrTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                   break;
                 }
               }
@@ -347,7 +372,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int qloc = 32 * (mq0 + m) + 8 * (r >> 2) + 4 * g + (r & 3);
-              __hip_atomic_store(dqt + (long long)qloc * D, dqAcc[m][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              __hip_atomic_store(dqt + (long long)qloc * D, dqAcc[m][r], __ATOMIC_RELAXED, kScope);
             }
         } else if constexpr (DQM == kDqOrderedAtomic) {
 #pragma unroll
@@ -359,19 +384,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
                                      __HIP_MEMORY_SCOPE_AGENT);
             }
         } else {
+          if constexpr (DQM == kDqLocalRmw) asm volatile("buffer_inv sc0" ::: "memory");
 #pragma unroll
           for (int m = 0; m < C::MQD; ++m) {
             float old[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int qloc = 32 * (mq0 + m) + 8 * (r >> 2) + 4 * g + (r & 3);
-              old[r] = __hip_atomic_load(dqt + (long long)qloc * D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              old[r] = __hip_atomic_load(dqt + (long long)qloc * D, __ATOMIC_RELAXED, kScope);
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int qloc = 32 * (mq0 + m) + 8 * (r >> 2) + 4 * g + (r & 3);
-              __hip_atomic_store(dqt + (long long)qloc * D, old[r] + dqAcc[m][r], __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
+              __hip_atomic_store(dqt + (long long)qloc * D, old[r] + dqAcc[m][r], __ATOMIC_RELAXED, kScope);
             }
           }
         }
@@ -393,25 +418,30 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
         }
       }
 
-      // ---- end of a column: publish, then dK, dV of KV tile j to global ----
-      int nj = -1;
-      if (t + 1 < len) {
-        int ni;
-        sc.tile(it, t + 1, ni, nj);
-      }
-      if (nj != j) {
-        wait_vm_all();
-        __syncthreads();
-        if (tid == 0 && pend_flag)
-          __hip_atomic_store(pend_flag, pend_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        pend_flag = nullptr;
-        float* red = reinterpret_cast<float*>(smem);
-        __bf16* sOut = reinterpret_cast<__bf16*>(smem + C::RED_BYTES);
-        store_column<C>(dKacc, a.scale, a.dk + head_off + (long long)j * BKV * D, red, sOut, wk, wq, lane);
-        store_column<C>(dVacc, 1.f, a.dv + head_off + (long long)j * BKV * D, red, sOut, wk, wq, lane);
-      }
+      ++t;
+      if (t >= t_end) break;
+      // the next tile's DMA (issued during this tile) and this tile's
+      // accumulator adds are complete in every wave
+      wait_vm_all();
+      __syncthreads();
+      if (tid == 0 && pend_flag)
+        __hip_atomic_store(pend_flag, pend_val, __ATOMIC_RELAXED, kFlagScope);
+      pend_flag = nullptr;
+    } while (true);  // tiles of the segment
+
+    // ---- end of a column: publish, then dK, dV of KV tile j to global ----
+    wait_vm_all();
+    __syncthreads();
+    if (tid == 0 && pend_flag) __hip_atomic_store(pend_flag, pend_val, __ATOMIC_RELAXED, kFlagScope);
+    pend_flag = nullptr;
+    {
+      float* red = reinterpret_cast<float*>(smem);
+      __bf16* sOut = reinterpret_cast<__bf16*>(smem + C::RED_BYTES);
+      store_column<C>(dKacc, a.scale, a.dk + head_off + (long long)j * BKV * D, red, sOut, wk, wq, lane);
+      store_column<C>(dVacc, 1.f, a.dv + head_off + (long long)j * BKV * D, red, sOut, wk, wq, lane);
     }
-  }
+    }  // segments
+  }  // items
 }
 
 }  // namespace detattn

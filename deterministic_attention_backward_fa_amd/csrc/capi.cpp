@@ -75,7 +75,7 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
   std::memset(&o, 0, sizeof(o));
   if (opt) o = *opt;
   if (o.block_q < 0 || o.block_kv < 0 || o.grid < 0 || o.xcd_remap < 0 || o.xcd_remap > 2 || o.dq_mode < 0 ||
-      o.dq_mode > 2)
+      o.dq_mode > 3)
     return DETATTN_ERR_INVALID_ARG;
   int bq, bkv;
   default_tiles(s.D, s.S, bq, bkv);
@@ -88,23 +88,21 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
   if (sch == DETATTN_SHIFT && causal) return DETATTN_ERR_UNSUPPORTED;
   if (sch == DETATTN_SYMMETRIC_SHIFT && (!causal || n_kv % 2 != 0)) return DETATTN_ERR_UNSUPPORTED;
 
-  int dqm = kDqUnordered;
-  int pub_dqm = 0;
-  if (sch != DETATTN_ATOMIC_NONDET) {
-    pub_dqm = o.dq_mode ? o.dq_mode : DETATTN_DQ_ORDERED_ATOMIC;
-    dqm = pub_dqm == DETATTN_DQ_ORDERED_ATOMIC ? kDqOrderedAtomic : kDqOrderedRmw;
-  }
-  const MainInfo info = s.D == 64 ? main_info_d64(bq, bkv, causal, dqm) : main_info_d128(bq, bkv, causal, dqm);
-  if (!info.func) return DETATTN_ERR_UNSUPPORTED;
+  // The kernel instance depends on the dQ mode, which depends on the ring
+  // placement below; occupancy (LDS-bound) is the same for every mode.
+  const MainInfo info0 = s.D == 64 ? main_info_d64(bq, bkv, causal, kDqOrderedRmw)
+                                   : main_info_d128(bq, bkv, causal, kDqOrderedRmw);
+  if (!info0.func) return DETATTN_ERR_UNSUPPORTED;
 
   const Sched sc{(int)sch, causal, n_q, n_kv, r};
   const long long BH = (long long)s.B * s.H;
   const long long items = BH * sc.items_per_head();
   int capacity = 0;  // co-resident workgroups
+  int cus = 0;
   if (o.grid == 0) {
-    const int cus = device_cus();
-    if (cus <= 0 || info.occupancy <= 0) return DETATTN_ERR_HIP;
-    capacity = cus * info.occupancy;
+    cus = device_cus();
+    if (cus <= 0 || info0.occupancy <= 0) return DETATTN_ERR_HIP;
+    capacity = cus * info0.occupancy;
   }
   const bool ring_sched = (sch == DETATTN_SHIFT || sch == DETATTN_SYMMETRIC_SHIFT);
   int grid = o.grid ? o.grid : capacity;
@@ -128,8 +126,24 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
     }
     grid = rings * ring;
   } else {
+    xcd = 0;
     if ((long long)grid > items) grid = (int)items;
   }
+
+  // dQ accumulation mode
+  int dqm = kDqUnordered;
+  int pub_dqm = 0;
+  if (sch != DETATTN_ATOMIC_NONDET) {
+    const bool local_ok = ring_sched && xcd;
+    pub_dqm = o.dq_mode;
+    if (pub_dqm == DETATTN_DQ_DEFAULT) pub_dqm = local_ok ? DETATTN_DQ_XCD_LOCAL_RMW : DETATTN_DQ_ORDERED_ATOMIC;
+    if (pub_dqm == DETATTN_DQ_XCD_LOCAL_RMW && !local_ok) return DETATTN_ERR_UNSUPPORTED;
+    dqm = pub_dqm == DETATTN_DQ_ORDERED_ATOMIC ? kDqOrderedAtomic
+          : pub_dqm == DETATTN_DQ_XCD_LOCAL_RMW ? kDqLocalRmw
+                                                 : kDqOrderedRmw;
+  }
+  const MainInfo info = s.D == 64 ? main_info_d64(bq, bkv, causal, dqm) : main_info_d128(bq, bkv, causal, dqm);
+  if (!info.func) return DETATTN_ERR_UNSUPPORTED;
   P.pub.block_q = bq;
   P.pub.block_kv = bkv;
   P.pub.n_q = n_q;
@@ -161,6 +175,7 @@ const char* detattn_status_string(int status) {
     case DETATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case DETATTN_ERR_HIP: return "HIP runtime error";
     case DETATTN_ERR_DEVICE_TIMEOUT: return "ordered dQ wait timed out on the device";
+    case DETATTN_ERR_DEVICE_PLACEMENT: return "a workgroup ran on an unexpected XCD (XCD-local dQ mode)";
     default: return "unknown status";
   }
 }
@@ -204,13 +219,15 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
   unsigned* header = reinterpret_cast<unsigned*>(ws);
   int* flags = reinterpret_cast<int*>(ws + L.flags_off);
   float* delta = reinterpret_cast<float*>(ws + L.delta_off);
+  float* lse2 = reinterpret_cast<float*>(ws + L.lse2_off);
   float* dqacc = reinterpret_cast<float*>(ws + L.dqacc_off);
   hipStream_t st_ = static_cast<hipStream_t>(stream);
   const long long rows = BH * s.S;
   const long long elems = rows * s.D;
   const bool unordered = P.dqm_internal == kDqUnordered;
 
-  hipError_t e = launch_pre(s.D, static_cast<const __bf16*>(o), static_cast<const __bf16*>(dout), delta, rows, flags,
+  hipError_t e = launch_pre(s.D, static_cast<const __bf16*>(o), static_cast<const __bf16*>(dout), lse, lse2, delta,
+                            rows, flags,
                             BH * P.pub.n_q, header, unordered ? dqacc : nullptr, elems, st_);
   if (e != hipSuccess) return DETATTN_ERR_HIP;
 
@@ -221,7 +238,7 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
   a.k = static_cast<const __bf16*>(k);
   a.v = static_cast<const __bf16*>(v);
   a.dout = static_cast<const __bf16*>(dout);
-  a.lse = lse;
+  a.lse2 = lse2;
   a.delta = delta;
   a.dqacc = dqacc;
   a.dk = static_cast<__bf16*>(dk);
@@ -274,7 +291,8 @@ int detattn_device_status(void* workspace, void* stream) {
   unsigned err = 0;
   const unsigned* header = static_cast<const unsigned*>(workspace);
   if (hipMemcpy(&err, header + 16, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess) return DETATTN_ERR_HIP;
-  return err == kErrNone ? DETATTN_OK : DETATTN_ERR_DEVICE_TIMEOUT;
+  if (err == kErrNone) return DETATTN_OK;
+  return (err & kErrTimeout) ? DETATTN_ERR_DEVICE_TIMEOUT : DETATTN_ERR_DEVICE_PLACEMENT;
 }
 
 int detattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, detattn_shape_t s,

@@ -31,6 +31,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -51,6 +53,9 @@ __device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) 
   r[3] = (__bf16)d;
   return r;
 }
+
+// Two fp32 -> two bf16 (RNE) with one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ bf16x2 cvt2(float a, float b) { return __builtin_convertvector(f32x2{a, b}, bf16x2); }
 
 // Eight accumulator registers [8h, 8h+8) of a C tile as a bf16 MFMA operand.
 __device__ __forceinline__ bf16x8 acc_slice_bf16(const f32x16& c, int h) {
@@ -197,20 +202,21 @@ struct WsLayout {
   static constexpr size_t kHeader = 256;         // ticket @0, error word @64, error detail @128
   static constexpr size_t kFlagStride = 128;     // one L2 line per dQ tile flag
   static constexpr size_t kMinBlockQ = 64;
-  size_t flags_off, flags_bytes, delta_off, delta_bytes, dqacc_off, dqacc_bytes, total;
+  size_t flags_off, flags_bytes, delta_off, delta_bytes, lse2_off, dqacc_off, dqacc_bytes, total;
   __host__ __device__ WsLayout(long long BH, long long S, long long D) {
     flags_off = kHeader;
     long long nq_max = (S + (long long)kMinBlockQ - 1) / (long long)kMinBlockQ;
     flags_bytes = (size_t)(BH * nq_max) * kFlagStride;
     delta_off = align(flags_off + flags_bytes);
     delta_bytes = (size_t)(BH * S) * 4;
-    dqacc_off = align(delta_off + delta_bytes);
+    lse2_off = align(delta_off + delta_bytes);  // LSE * log2(e), same size as delta
+    dqacc_off = align(lse2_off + delta_bytes);
     dqacc_bytes = (size_t)(BH * S * D) * 4;
     total = align(dqacc_off + dqacc_bytes);
   }
   __host__ __device__ static size_t align(size_t x) { return (x + 255) & ~(size_t)255; }
 };
 
-enum DeviceError : uint32_t { kErrNone = 0, kErrTimeout = 1 };
+enum DeviceError : uint32_t { kErrNone = 0, kErrTimeout = 1, kErrPlacement = 2 };
 
 }  // namespace detattn

@@ -43,6 +43,17 @@ struct Sched {
     }
   }
 
+  // An item visits one KV tile (one segment) or, for symmetric shift, two KV
+  // tiles one after the other (two segments); segments split the item's tile
+  // sequence at the column switch.
+  __host__ __device__ __forceinline__ int segments() const { return sch == kSymmetricShift ? 2 : 1; }
+  __host__ __device__ __forceinline__ int seg_begin(int it, int seg) const {
+    return seg == 0 ? 0 : n_q - it * r;  // symmetric: column p holds n_q - p*r tiles
+  }
+  __host__ __device__ __forceinline__ int seg_end(int it, int seg) const {
+    return (sch == kSymmetricShift && seg == 0) ? n_q - it * r : item_len(it);
+  }
+
   // The t-th tile (0 <= t < item_len(it)) of item `it`.
   __host__ __device__ __forceinline__ void tile(int it, int t, int& i, int& j) const {
     switch (sch) {

@@ -79,14 +79,18 @@ typedef enum {
   DETATTN_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement */
   DETATTN_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
   DETATTN_ERR_HIP = 4,           /* a HIP runtime call failed (launch, copy, sync) */
-  DETATTN_ERR_DEVICE_TIMEOUT = 5 /* an ordered dQ wait timed out on the device */
+  DETATTN_ERR_DEVICE_TIMEOUT = 5, /* an ordered dQ wait timed out on the device */
+  DETATTN_ERR_DEVICE_PLACEMENT = 6 /* XCD-local mode: a workgroup ran on an unexpected XCD */
 } detattn_status_t;
 
 /* dQ accumulation mechanism for the ordered schedules. */
 typedef enum {
   DETATTN_DQ_DEFAULT = 0,
   DETATTN_DQ_ORDERED_RMW = 1,   /* load + add + store of the fp32 accumulator, in rank order */
-  DETATTN_DQ_ORDERED_ATOMIC = 2 /* fp32 atomic adds issued in rank order (same order, same bits per run) */
+  DETATTN_DQ_ORDERED_ATOMIC = 2, /* fp32 atomic adds issued in rank order (same order, same bits per run) */
+  DETATTN_DQ_XCD_LOCAL_RMW = 3   /* ring schedules whose ring fits one XCD: read-modify-write and flags kept
+                                    coherent in that XCD's L2 (never leave it during the kernel); the
+                                    library checks the workgroup-to-XCD placement on the device */
 } detattn_dq_mode_t;
 
 /*
@@ -160,7 +164,8 @@ int detattn_bwd_plan(detattn_shape_t shape, detattn_mask_t mask, detattn_schedul
                      const detattn_bwd_options_t* options, detattn_plan_t* plan);
 
 /* Synchronise `stream` and read the device error word of the last call that
- * used `workspace`: DETATTN_OK or DETATTN_ERR_DEVICE_TIMEOUT (or ERR_HIP). */
+ * used `workspace`: DETATTN_OK, DETATTN_ERR_DEVICE_TIMEOUT or
+ * DETATTN_ERR_DEVICE_PLACEMENT (or ERR_HIP). */
 int detattn_device_status(void* workspace, void* stream);
 
 /* Static, human-readable name of a status code. */

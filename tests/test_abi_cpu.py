@@ -33,7 +33,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(6):
+    for code in range(7):
         assert da.status_string(code) and da.status_string(code) != "unknown status"
     assert da.status_string(99) == "unknown status"
 

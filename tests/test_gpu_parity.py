@@ -108,7 +108,8 @@ def test_invariance_grid_placement_delays(case):
         base = [t.clone() for t in da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule=sched,
                                                             workspace=ws, **opts)]
         plan = da.detattn_bwd_plan(B, H, S, D, causal, sched, **opts)
-        variants = [dict(debug_delay_seed=12345), dict(xcd_remap=False), dict(dq_mode="atomic")]
+        variants = [dict(debug_delay_seed=12345), dict(xcd_remap=False), dict(dq_mode="atomic"),
+                    dict(dq_mode="rmw")]
         ring = plan["ring"]
         if ring:
             variants.append(dict(grid=ring))           # a single ring at a time
@@ -120,13 +121,14 @@ def test_invariance_grid_placement_delays(case):
             got = da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule=sched, workspace=ws,
                                             **opts, **var)
             assert da.detattn_device_status(ws) == 0
-            if var.get("dq_mode") == "atomic":
-                # hardware fp32 atomic adds in the same order: same dK/dV bits, dQ within tolerance
-                assert same_bits(base[1], got[1]) and same_bits(base[2], got[2])
-                assert rel_err(got[0].float().cpu().numpy(), base[0].float().cpu().numpy()) <= 1e-2
+            # dK and dV never depend on the dQ mechanism or placement
+            assert same_bits(base[1], got[1]) and same_bits(base[2], got[2]), (sched, var)
+            vplan = da.detattn_bwd_plan(B, H, S, D, causal, sched, **opts, **var)
+            if vplan["dq_mode"] == plan["dq_mode"]:
+                assert same_bits(base[0], got[0]), (sched, var)
             else:
-                for a, b in zip(base, got):
-                    assert same_bits(a, b), (sched, var)
+                # same order, another add mechanism (VALU add vs fp32 atomic): equal up to rounding of denormals
+                assert rel_err(got[0].float().cpu().numpy(), base[0].float().cpu().numpy()) <= 1e-2
 
 
 def test_timeout_path_reports_and_exits():
