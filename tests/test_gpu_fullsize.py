@@ -1,0 +1,82 @@
+"""Full-size GPU checks in the launch configuration the benchmark times.
+
+For every workload shape below, every valid schedule runs with the library's
+default plan (tiles, grid, rings, dQ mode). The fp64 oracle computes sampled
+outputs one by one on two heads (the first and the last): dQ at sampled query
+rows, dK and dV at sampled key rows, plus every row's log-sum-exp. The bar is
+the same as for the small cases, max|gpu - oracle| <= 2e-2 * max|oracle| over
+the sampled values, and the bitwise relations between schedules that share an
+accumulation order hold at full size. The long-context shapes also repeat
+every schedule 100 times and require identical bits.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import deterministic_attention_backward_fa_amd as da
+from deterministic_attention_backward_fa_amd.synth import make_qkvdo, sample_indices
+from oracle import ref as oref
+
+from gpu_util import TOL, rel_err, same_bits, say
+
+pytestmark = pytest.mark.gpu
+
+CONFIGS = {
+    # name: (B, H, S, D, causal, seed, runs for the determinism check)
+    "causal_b4_h16_s2048_d64": (4, 16, 2048, 64, True, 102, 3),
+    "full_b2_h32_s4096_d128": (2, 32, 4096, 128, False, 103, 3),
+    "causal_b1_h32_s8192_d128": (1, 32, 8192, 128, True, 104, 3),
+    "full_b1_h16_s16384_d128": (1, 16, 16384, 128, False, 105, 100),
+    "causal_b1_h16_s16384_d128": (1, 16, 16384, 128, True, 105, 100),
+}
+
+
+def schedules_for(causal):
+    return ["serial_ascending", "descending_q", "symmetric_shift" if causal else "shift", "atomic_nondet"]
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_fullsize_sampled_parity_and_determinism(name):
+    B, H, S, D, causal, seed, runs = CONFIGS[name]
+    scale = 1.0 / math.sqrt(D)
+    say(f"[fullsize] {name}: inputs")
+    cpu = make_qkvdo(B, H, S, D, seed)
+    q, k, v, do = (t.cuda() for t in cpu)
+    o, lse = da.detattn_fwd(q, k, v, causal=causal)
+    torch.cuda.synchronize()
+    rows = sample_indices(S, 12, seed)
+    cols = sample_indices(S, 12, seed + 1)
+    heads = [(0, 0), (B - 1, H - 1)]
+    refs = {}
+    for (b, h) in heads:
+        say(f"[fullsize] {name}: oracle head ({b},{h})")
+        refs[(b, h)] = oref.attn_bwd_sampled(cpu[0][b, h], cpu[1][b, h], cpu[2][b, h], cpu[3][b, h], scale, causal,
+                                             rows, cols)
+        # forward statistics of the library against the oracle's, every row
+        assert np.max(np.abs(lse[b, h].cpu().numpy() - refs[(b, h)][3])) <= 1e-3
+    outs = {}
+    for sched in schedules_for(causal):
+        say(f"[fullsize] {name}: {sched} plan {da.detattn_bwd_plan(B, H, S, D, causal, sched)}")
+        ws = da.alloc_workspace(B, H, S, D)
+        first = [t.clone() for t in da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule=sched,
+                                                             workspace=ws)]
+        assert da.detattn_device_status(ws) == 0
+        for (b, h) in heads:
+            rdq, rdk, rdv, _, _ = refs[(b, h)]
+            for label, got, want in (("dq", first[0][b, h, rows], rdq), ("dk", first[1][b, h, cols], rdk),
+                                     ("dv", first[2][b, h, cols], rdv)):
+                e = rel_err(got.float().cpu().numpy(), want)
+                assert e <= TOL, f"{name} {sched} head ({b},{h}) {label}: rel err {e:.3e}"
+        if sched != "atomic_nondet":
+            out = tuple(torch.empty_like(t) for t in first)
+            for _ in range(runs - 1):
+                da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule=sched, workspace=ws, out=out)
+                for a, b_ in zip(first, out):
+                    assert same_bits(a, b_), f"{name} {sched} not bit-identical across runs"
+            assert da.detattn_device_status(ws) == 0
+        outs[sched] = first
+    assert same_bits(outs["serial_ascending"][0], outs["descending_q"][0])
+    assert same_bits(outs["serial_ascending"][1], outs["atomic_nondet"][1])
+    assert same_bits(outs["serial_ascending"][2], outs["atomic_nondet"][2])
