@@ -61,6 +61,37 @@ class HipEvents:
         self.hip.hipEventDestroy(e)
 
 
+def kernel_source_hash():
+    """sha256 over the HIP library sources: identifies the kernel build a profile was taken on."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "deterministic_attention_backward_fa_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "detattn.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def profiled_traffic(config_name):
+    """HBM bytes per main-kernel launch from the committed rocprofv3 PMC summary of this
+    workload, or None when there is none or the kernel sources changed since it was taken."""
+    import re
+
+    path = os.path.join(ROOT, "profiles", f"bwd_main_{config_name}.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\s*(\{.*?\})\s*```", open(path).read(), flags=re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec
+
+
 def counted_flops(B, H, S, D, causal):
     f = 10.0 * B * H * S * S * D
     return f / 2 if causal else f
@@ -139,6 +170,7 @@ def main():
     ap.add_argument("--only-headline", action="store_true", help="skip the other schedules")
     ap.add_argument("--dq-mode", default="default", choices=["default", "rmw", "atomic", "xcd_local"],
                     help="ordered dQ accumulation mechanism for the deterministic schedules")
+    ap.add_argument("--trace", action="store_true", help="log the headline schedule's per-tile phase breakdown")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -189,6 +221,7 @@ def main():
     algo_flops = 10.0 * plan["block_q"] * plan["block_kv"] * D * tiles
     achieved = algo_flops / (head["main_ms"] * 1e-3) / 1e12
     atomic = results.get("atomic_nondet")
+    traffic = profiled_traffic(args.config)
     line = {
         "metric": "deterministic attn-bwd TFLOP/s (bf16, full+causal) and ratio vs atomic nondet",
         "value": round(head["tflops"], 2),
@@ -211,10 +244,21 @@ def main():
                           "ratio_vs_atomic": round(r["tflops"] / atomic["tflops"], 4) if atomic else None}
                       for s, r in results.items()},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic["hbm_bytes_per_launch"] if traffic else None,
+                     "traffic_detail": traffic,
                      "kernel": "bwd_main_kernel", "algorithmic_flops_per_launch": algo_flops,
                      "avg_launch_ms": round(head["main_ms"], 4)},
     }
+    if args.trace:
+        from deterministic_attention_backward_fa_amd import trace as dtrace
+
+        recs, _ = dtrace.collect(da, tensors, causal, headline)
+        summ = dtrace.summarize(recs)
+        log(f"[bench] trace {headline}: {summ['mean_ticks_per_tile']:.0f} ticks/tile over {summ['workgroups']} WGs")
+        for name, share in summ["share"].items():
+            log(f"[bench]   {share * 100:5.1f}%  {summ['ticks'][name]:8.0f}  {name}")
+        line["trace_share"] = {k: round(v, 4) for k, v in summ["share"].items()}
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: fp64 oracle on a bounded sample")
         line["cpu_baseline"] = cpu_baseline((B, H, S, D), causal, seed)

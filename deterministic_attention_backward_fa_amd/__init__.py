@@ -35,7 +35,8 @@ class BwdOptions(ctypes.Structure):
     _fields_ = [("block_q", ctypes.c_int32), ("block_kv", ctypes.c_int32), ("grid", ctypes.c_int32),
                 ("xcd_remap", ctypes.c_int32), ("dq_mode", ctypes.c_int32), ("debug_delay_seed", ctypes.c_uint32),
                 ("timeout_us", ctypes.c_uint32), ("debug_skip_signal", ctypes.c_int32),
-                ("main_begin_event", ctypes.c_void_p), ("main_end_event", ctypes.c_void_p)]
+                ("main_begin_event", ctypes.c_void_p), ("main_end_event", ctypes.c_void_p),
+                ("trace", ctypes.c_void_p), ("trace_records", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -119,10 +120,11 @@ def _check_tensor(name, t, dtype, shape):
 
 
 def _options(block_q=0, block_kv=0, grid=0, xcd_remap=None, dq_mode="default", debug_delay_seed=0, timeout_us=0,
-             debug_skip_signal=0, main_begin_event=None, main_end_event=None):
+             debug_skip_signal=0, main_begin_event=None, main_end_event=None, trace=None, trace_records=0):
     xr = 0 if xcd_remap is None else (1 if xcd_remap else 2)
     return BwdOptions(int(block_q), int(block_kv), int(grid), xr, DQ_MODES[dq_mode], int(debug_delay_seed),
-                      int(timeout_us), int(debug_skip_signal), main_begin_event, main_end_event)
+                      int(timeout_us), int(debug_skip_signal), main_begin_event, main_end_event,
+                      trace.data_ptr() if trace is not None else None, int(trace_records))
 
 
 def detattn_fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):

@@ -49,6 +49,8 @@ struct BwdArgs {
   long long timeout_ticks;  // s_memrealtime ticks (100 MHz)
   unsigned delay_seed;
   int skip_item;       // testing: global item index whose first signal is withheld, or -1
+  unsigned long long* trace;  // optional per-workgroup phase timestamps
+  int trace_records;
 };
 
 static constexpr int kFlagInts = (int)(WsLayout::kFlagStride / 4);

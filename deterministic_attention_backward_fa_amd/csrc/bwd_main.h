@@ -184,6 +184,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     dma_f32(ld + BQ, a.delta + bhS + qrow0, BQ, 1);
   };
 
+  // Optional phase trace: wave 0, lane 0 of each workgroup.
+  int trace_n = 0;
+  auto trace_rec = [&](int phase, int t, long long item) {
+    if (a.trace && tid == 0 && trace_n < a.trace_records) {
+      unsigned long long* p = a.trace + ((size_t)blockIdx.x * a.trace_records + trace_n) * 2;
+      p[0] = __builtin_amdgcn_s_memtime();
+      p[1] = (unsigned long long)phase | ((unsigned long long)(t & 0xFFFFFF) << 8) | ((unsigned long long)item << 32);
+      ++trace_n;
+    }
+  };
+
   for (long long round = 0;; ++round) {
     long long gidx;
     if (a.ticket_mode) {
@@ -216,18 +227,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     dma_q(0, head_off, bhS, i0);
     wait_vm_all();
     __syncthreads();
-    bf16x8 kB[C::KD], vB[C::KD];
+    bf16x8 kB[C::KD], vB[C::KD], kTB[C::KKV];
 #pragma unroll
     for (int s = 0; s < C::KD; ++s) {
       kB[s] = frag_row_s<C::NCH_D>(sK, 32 * wk, 16 * s);
       vB[s] = frag_row_s<C::NCH_D>(sV, 32 * wk, 16 * s);
     }
+#pragma unroll
+    for (int s = 0; s < C::KKV; ++s) kTB[s] = frag_tr_s<C::NCH_D>(sK, 16 * s, 32 * nbq, false);
     f32x16 dKacc[C::ND], dVacc[C::ND];
 #pragma unroll
     for (int n = 0; n < C::ND; ++n) {
       dKacc[n] = f32x16{};
       dVacc[n] = f32x16{};
     }
+    trace_rec(6, t_begin, gidx);
 
     int t = t_begin;
     do {
@@ -235,6 +249,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       sc.tile(it, t, i, jj);
       const int b = (t - t_begin) & 1;
       const long long qrow0 = (long long)i * BQ;
+      trace_rec(0, t, gidx);
       // prefetch the next tile of this column into the other buffer
       if (t + 1 < t_end) {
         int ni, nj;
@@ -246,64 +261,80 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       const float* sL = reinterpret_cast<const float*>(smem + (b ? C::OFF_LD1 : C::OFF_LD0));
       const float* sDl = sL + BQ;
 
-      // ---- S = Q K^T and dP = dO V^T for this wave's (QW x 32) block ----
+      // Per 32-row block mb of this wave's Q rows the work is: S and dP
+      // (2*KD MFMAs), the elementwise P/dS (VALU), and dV/dK over the block's
+      // two K steps (4*ND MFMAs). Blocks are pipelined so that the MFMAs of one
+      // block run while the VALU of the previous one executes; the last
+      // block's dV/dK is deferred until after the dQ hand-off, where it covers
+      // the latency of the accumulator adds.
+      const bool diag = CAUSAL && ((long long)(j + 1) * BKV - 1 > qrow0);
+      // kv - q offset of this lane's column against the tile's first Q row;
+      // pushed far below any q when the tile needs no mask (branch-free).
+      const int kv_rel = diag ? (int)((long long)j * BKV - qrow0) + 32 * wk + c32 : -(1 << 30);
       f32x16 sAcc[C::MQ], pAcc[C::MQ];
-#pragma unroll
-      for (int mb = 0; mb < C::MQ; ++mb) {
+      bf16x8 pB[C::KQ], dsB[C::KQ];
+
+      auto sdp = [&](int mb) {
         sAcc[mb] = f32x16{};
         pAcc[mb] = f32x16{};
-      }
 #pragma unroll
-      for (int s = 0; s < C::KD; ++s) {
-#pragma unroll
-        for (int mb = 0; mb < C::MQ; ++mb) {
+        for (int s = 0; s < C::KD; ++s) {
           const bf16x8 aq = frag_row_s<C::NCH_D>(sQ, C::QW * wq + 32 * mb, 16 * s);
           sAcc[mb] = mfma32(aq, kB[s], sAcc[mb]);
           const bf16x8 ad = frag_row_s<C::NCH_D>(sdO, C::QW * wq + 32 * mb, 16 * s);
           pAcc[mb] = mfma32(ad, vB[s], pAcc[mb]);
         }
-      }
-
-      // ---- P and dS (C layout: row q, column kv = lane) ----
-      // Only tiles that straddle the diagonal need the causal mask.
-      const bool diag = CAUSAL && ((long long)(j + 1) * BKV - 1 > qrow0);
-      bf16x8 pB[C::KQ], dsB[C::KQ];
-      auto elementwise = [&](auto masked) {
-        const int kv_rel = (int)((long long)j * BKV - qrow0) + 32 * wk + c32;  // kv - first q of the tile
+      };
+      auto elem = [&](int mb) {
 #pragma unroll
-        for (int mb = 0; mb < C::MQ; ++mb) {
+        for (int rq = 0; rq < 4; ++rq) {
+          const int qloc = C::QW * wq + 32 * mb + 8 * rq + 4 * g;
+          const f32x4 L4 = *reinterpret_cast<const f32x4*>(sL + qloc);
+          const f32x4 D4 = *reinterpret_cast<const f32x4*>(sDl + qloc);
+          float p[4], ds[4];
 #pragma unroll
-          for (int rq = 0; rq < 4; ++rq) {
-            const int qloc = C::QW * wq + 32 * mb + 8 * rq + 4 * g;
-            const f32x4 L4 = *reinterpret_cast<const f32x4*>(sL + qloc);
-            const f32x4 D4 = *reinterpret_cast<const f32x4*>(sDl + qloc);
-            float p[4], ds[4];
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * rq + e;
+            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sAcc[mb][r], c1, -L4[e]));
+            p[e] = kv_rel > qloc + e ? 0.f : p[e];
+            ds[e] = p[e] * (pAcc[mb][r] - D4[e]);
+          }
+          const int kstep = 2 * mb + (rq >> 1);
+          const int sl = 4 * (rq & 1);
+          const bf16x2 p01 = cvt2(p[0], p[1]), p23 = cvt2(p[2], p[3]);
+          const bf16x2 d01 = cvt2(ds[0], ds[1]), d23 = cvt2(ds[2], ds[3]);
+          pB[kstep][sl] = p01[0];
+          pB[kstep][sl + 1] = p01[1];
+          pB[kstep][sl + 2] = p23[0];
+          pB[kstep][sl + 3] = p23[1];
+          dsB[kstep][sl] = d01[0];
+          dsB[kstep][sl + 1] = d01[1];
+          dsB[kstep][sl + 2] = d23[0];
+          dsB[kstep][sl + 3] = d23[1];
+        }
+      };
+      auto dvdk = [&](int mb) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * rq + e;
-              p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sAcc[mb][r], c1, -L4[e]));
-              if constexpr (decltype(masked)::value) {
-                if (kv_rel > qloc + e) p[e] = 0.f;
-              }
-              ds[e] = p[e] * (pAcc[mb][r] - D4[e]);
-            }
-            const int kstep = 2 * mb + (rq >> 1);
-            const int sl = 4 * (rq & 1);
-            const bf16x2 p01 = cvt2(p[0], p[1]), p23 = cvt2(p[2], p[3]);
-            const bf16x2 d01 = cvt2(ds[0], ds[1]), d23 = cvt2(ds[2], ds[3]);
-            pB[kstep][sl] = p01[0];
-            pB[kstep][sl + 1] = p01[1];
-            pB[kstep][sl + 2] = p23[0];
-            pB[kstep][sl + 3] = p23[1];
-            dsB[kstep][sl] = d01[0];
-            dsB[kstep][sl + 1] = d01[1];
-            dsB[kstep][sl + 2] = d23[0];
-            dsB[kstep][sl + 3] = d23[1];
+        for (int s = 2 * mb; s < 2 * mb + 2; ++s) {
+#pragma unroll
+          for (int n = 0; n < C::ND; ++n) {
+            const bf16x8 bo = frag_tr_s<C::NCH_D>(sdO, C::QW * wq + 16 * s, 32 * n, true);
+            dVacc[n] = mfma32(pB[s], bo, dVacc[n]);
+            const bf16x8 bq = frag_tr_s<C::NCH_D>(sQ, C::QW * wq + 16 * s, 32 * n, true);
+            dKacc[n] = mfma32(dsB[s], bq, dKacc[n]);
           }
         }
       };
-      if (diag) elementwise(std::true_type{});
-      else elementwise(std::false_type{});
+
+      sdp(0);
+#pragma unroll
+      for (int mb = 1; mb < C::MQ; ++mb) {
+        sdp(mb);
+        elem(mb - 1);
+        if (mb >= 2) dvdk(mb - 2);
+      }
+      elem(C::MQ - 1);
+      if (C::MQ >= 2) dvdk(C::MQ - 2);
 
       // ---- dS^T -> LDS (row kv, column q), 4 consecutive q per 8-byte store ----
 #pragma unroll
@@ -317,6 +348,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
           *reinterpret_cast<bf16x4*>(sdS + swz_off<C::NCH_S>(32 * wk + c32, q0)) = v4;
         }
       }
+      trace_rec(1, t, gidx);
+
+      // The dQ tile's flag is read now; the load completes under the barrier
+      // and the dQ MFMAs, and is only re-polled if the turn has not come yet.
+      const int rk = DQM == kDqUnordered ? 0 : sc.rank(i, j);
+      int* flag = a.flags + ((long long)bh * sc.n_q + i) * kFlagInts;
+      int seen = rk;
+      if (DQM != kDqUnordered && rk > 0 && lane == 0) seen = __hip_atomic_load(flag, __ATOMIC_RELAXED, kFlagScope);
       __syncthreads();
 
       // ---- dQ partial = dS K (this wave's D block, MQD row blocks) ----
@@ -328,29 +367,29 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
         for (int m = 0; m < C::MQD; ++m) {
           const bf16x8 ad = frag_tr_s<C::NCH_S>(sdS, 16 * s, 32 * (mq0 + m), false);
-          dqAcc[m] = mfma32(ad, frag_tr_s<C::NCH_D>(sK, 16 * s, 32 * nbq, false), dqAcc[m]);
+          dqAcc[m] = mfma32(ad, kTB[s], dqAcc[m]);
         }
       }
+      trace_rec(2, t, gidx);
 
       // ---- add the partial into dQ tile i's fp32 accumulator ----
       float* dqt = a.dqacc + head_off + qrow0 * D + 32 * nbq + c32;
       if constexpr (DQM == kDqUnordered) {
+        __builtin_amdgcn_sched_barrier(0);  // same scheduling region boundary as the ordered modes' turn wait
 #pragma unroll
         for (int m = 0; m < C::MQD; ++m)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int qloc = 32 * (mq0 + m) + 8 * (r >> 2) + 4 * g + (r & 3);
-            atomicAdd(dqt + (long long)qloc * D, dqAcc[m][r]);
+            __hip_atomic_fetch_add(dqt + (long long)qloc * D, dqAcc[m][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
       } else {
-        const int rk = sc.rank(i, j);
-        int* flag = a.flags + ((long long)bh * sc.n_q + i) * kFlagInts;
         if (lane == 0) {
           if (a.delay_seed) {
             const long long until = now_ticks() + (hash3(a.delay_seed, (unsigned)gidx, (unsigned)(t * 4 + w)) & 1023u);
             while (now_ticks() < until) __builtin_amdgcn_s_sleep(2);
           }
-          if (rk > 0) {
+          if (seen != rk) {
             const long long t0 = now_ticks();
             int spins = 0;
             while (__hip_atomic_load(flag, __ATOMIC_RELAXED, kFlagScope) != rk) {
@@ -366,6 +405,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
           }
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        trace_rec(3, t, gidx);
         if (rk == 0) {
 #pragma unroll
           for (int m = 0; m < C::MQD; ++m)
@@ -385,39 +425,32 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
             }
         } else {
           if constexpr (DQM == kDqLocalRmw) asm volatile("buffer_inv sc0" ::: "memory");
+          float old[C::MQD][16];
 #pragma unroll
-          for (int m = 0; m < C::MQD; ++m) {
-            float old[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int qloc = 32 * (mq0 + m) + 8 * (r >> 2) + 4 * g + (r & 3);
-              old[r] = __hip_atomic_load(dqt + (long long)qloc * D, __ATOMIC_RELAXED, kScope);
-            }
+          for (int m = 0; m < C::MQD; ++m)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int qloc = 32 * (mq0 + m) + 8 * (r >> 2) + 4 * g + (r & 3);
-              __hip_atomic_store(dqt + (long long)qloc * D, old[r] + dqAcc[m][r], __ATOMIC_RELAXED, kScope);
+              old[m][r] = __hip_atomic_load(dqt + (long long)qloc * D, __ATOMIC_RELAXED, kScope);
             }
-          }
+#pragma unroll
+          for (int m = 0; m < C::MQD; ++m)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int qloc = 32 * (mq0 + m) + 8 * (r >> 2) + 4 * g + (r & 3);
+              __hip_atomic_store(dqt + (long long)qloc * D, old[m][r] + dqAcc[m][r], __ATOMIC_RELAXED, kScope);
+            }
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         const bool withhold = (a.skip_item >= 0 && gidx == a.skip_item && t == 0);
         pend_flag = withhold ? nullptr : flag;
         pend_val = rk + 1;
       }
+      trace_rec(4, t, gidx);
+      // the last block's dV/dK runs while the adds are in flight
+      dvdk(C::MQ - 1);
 
-      // ---- dV += P^T dO, dK += dS^T Q (while the adds are in flight) ----
-#pragma unroll
-      for (int s = 0; s < C::KQ; ++s) {
-#pragma unroll
-        for (int n = 0; n < C::ND; ++n) {
-          const bf16x8 bo = frag_tr_s<C::NCH_D>(sdO, C::QW * wq + 16 * s, 32 * n, true);
-          dVacc[n] = mfma32(pB[s], bo, dVacc[n]);
-          const bf16x8 bq = frag_tr_s<C::NCH_D>(sQ, C::QW * wq + 16 * s, 32 * n, true);
-          dKacc[n] = mfma32(dsB[s], bq, dKacc[n]);
-        }
-      }
-
+      trace_rec(5, t, gidx);
       ++t;
       if (t >= t_end) break;
       // the next tile's DMA (issued during this tile) and this tile's
@@ -440,6 +473,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       store_column<C>(dKacc, a.scale, a.dk + head_off + (long long)j * BKV * D, red, sOut, wk, wq, lane);
       store_column<C>(dVacc, 1.f, a.dv + head_off + (long long)j * BKV * D, red, sOut, wk, wq, lane);
     }
+    trace_rec(7, t_end, gidx);
     }  // segments
   }  // items
 }

@@ -208,6 +208,9 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
   const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
   for (const void* p : ptrs)
     if (!p || !aligned16(p)) return DETATTN_ERR_INVALID_ARG;
+  if (options && options->trace &&
+      (options->trace_records <= 0 || (reinterpret_cast<uintptr_t>(options->trace) & 7u) != 0))
+    return DETATTN_ERR_INVALID_ARG;
   Plan P;
   const int st = make_plan(s, mask, schedule, options, P);
   if (st != DETATTN_OK) return st;
@@ -257,6 +260,10 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
   a.timeout_ticks = P.timeout_ticks;
   a.delay_seed = options ? options->debug_delay_seed : 0u;
   a.skip_item = (options && options->debug_skip_signal > 0) ? options->debug_skip_signal - 1 : -1;
+  if (options && options->trace) {
+    a.trace = reinterpret_cast<unsigned long long*>(options->trace);
+    a.trace_records = options->trace_records;
+  }
   M.D = s.D;
   M.BQ = P.pub.block_q;
   M.BKV = P.pub.block_kv;

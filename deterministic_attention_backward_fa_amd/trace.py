@@ -1,0 +1,57 @@
+"""Per-tile phase timeline of the main kernel (the optional device trace).
+
+`collect` runs one attn_bwd_deterministic call with a trace buffer; every
+workgroup's wave 0 records (s_memtime, phase | tile << 8 | item << 32) at the
+phase boundaries listed in detattn_trace_phase_t. `summarize` turns the
+records into the mean share of each phase per tile, which shows where a
+schedule's time goes on the hardware (compute, waiting for the dQ tile's turn,
+accumulator adds, barriers).
+"""
+import numpy as np
+import torch
+
+PHASES = {0: "tile_top", 1: "ds_ready", 2: "dq_done", 3: "turn", 4: "adds_issued", 5: "tile_end", 6: "seg_begin",
+          7: "seg_end"}
+# consecutive phase pairs inside one tile, and the name of the interval
+INTERVALS = [
+    (0, 1, "S,dP MFMA + P,dS VALU + dS^T store"),
+    (1, 2, "barrier + dQ MFMA issue"),
+    (2, 3, "wait for the dQ tile's turn"),
+    (3, 4, "accumulator adds issued"),
+    (4, 5, "dV,dK MFMA issue"),
+    (5, 0, "drain + barrier + publish (to next tile)"),
+]
+
+
+def collect(da, tensors, causal, schedule, records=4096, **opts):
+    q, k, v, o, do, lse = tensors
+    B, H, S, D = q.shape
+    plan = da.detattn_bwd_plan(B, H, S, D, causal, schedule, **opts)
+    buf = torch.zeros(plan["grid"] * records * 2, dtype=torch.int64, device=q.device)
+    ws = da.alloc_workspace(B, H, S, D)
+    da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule=schedule, workspace=ws, trace=buf,
+                              trace_records=records, **opts)
+    torch.cuda.synchronize()
+    return buf.view(plan["grid"], records, 2).cpu().numpy(), plan
+
+
+def summarize(recs):
+    """Mean ticks per tile of each interval, over every workgroup's complete tiles."""
+    sums = {name: [] for _, _, name in INTERVALS}
+    spans = []
+    for wg in range(recs.shape[0]):
+        r = recs[wg]
+        r = r[r[:, 0] != 0]
+        if len(r) < 2:
+            continue
+        t = r[:, 0].astype(np.int64)
+        ph = (r[:, 1] & 0xFF).astype(np.int64)
+        spans.append(t[-1] - t[0])
+        for x in range(len(r) - 1):
+            for a, b, name in INTERVALS:
+                if ph[x] == a and ph[x + 1] == b:
+                    sums[name].append(t[x + 1] - t[x])
+    out = {name: (float(np.mean(v)) if v else 0.0) for name, v in sums.items()}
+    total = sum(out.values())
+    return {"mean_ticks_per_tile": total, "share": {k: (v / total if total else 0.0) for k, v in out.items()},
+            "ticks": out, "workgroups": len(spans)}

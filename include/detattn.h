@@ -110,7 +110,23 @@ typedef struct {
                                 failure path; every kernel still exits) */
   void* main_begin_event;    /* optional hipEvent_t recorded on `stream` right before the main kernel */
   void* main_end_event;      /* optional hipEvent_t recorded on `stream` right after the main kernel */
+  uint64_t* trace;           /* optional device buffer of grid * trace_records * 2 uint64: per workgroup, records
+                                (s_memtime, phase | tile << 8 | item << 32) at the phase boundaries of each
+                                tile (detattn_trace_phase_t); unused records stay as the caller left them */
+  int32_t trace_records;     /* records per workgroup in `trace` */
 } detattn_bwd_options_t;
+
+/* Phase ids written into the optional trace (low 8 bits of the second word). */
+typedef enum {
+  DETATTN_TRACE_TILE_TOP = 0,    /* tile inputs resident, previous flag published */
+  DETATTN_TRACE_DS_READY = 1,    /* P, dS computed and dS^T stored in LDS */
+  DETATTN_TRACE_DQ_DONE = 2,     /* dQ partial computed (after the dS barrier) */
+  DETATTN_TRACE_TURN = 3,        /* the dQ tile's flag reached this tile's rank */
+  DETATTN_TRACE_ADDS_ISSUED = 4, /* accumulator adds issued */
+  DETATTN_TRACE_TILE_END = 5,    /* dV/dK products issued */
+  DETATTN_TRACE_SEG_BEGIN = 6,   /* a KV column starts (K, V staged) */
+  DETATTN_TRACE_SEG_END = 7      /* its dK, dV stored */
+} detattn_trace_phase_t;
 
 /* What the library chose for a call (see detattn_bwd_plan). */
 typedef struct {
