@@ -274,15 +274,27 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       f32x16 sAcc[C::MQ], pAcc[C::MQ];
       bf16x8 pB[C::KQ], dsB[C::KQ];
 
+      // Operand fragments are software-pipelined one K step ahead: the loads
+      // of step s+1 are issued before the MFMAs of step s (sched_barrier keeps
+      // the compiler from regrouping them), so LDS latency overlaps the MFMAs.
       auto sdp = [&](int mb) {
         sAcc[mb] = f32x16{};
         pAcc[mb] = f32x16{};
+        bf16x8 aq = frag_row_s<C::NCH_D>(sQ, C::QW * wq + 32 * mb, 0);
+        bf16x8 ad = frag_row_s<C::NCH_D>(sdO, C::QW * wq + 32 * mb, 0);
 #pragma unroll
         for (int s = 0; s < C::KD; ++s) {
-          const bf16x8 aq = frag_row_s<C::NCH_D>(sQ, C::QW * wq + 32 * mb, 16 * s);
+          bf16x8 aqn = aq, adn = ad;
+          if (s + 1 < C::KD) {
+            aqn = frag_row_s<C::NCH_D>(sQ, C::QW * wq + 32 * mb, 16 * (s + 1));
+            adn = frag_row_s<C::NCH_D>(sdO, C::QW * wq + 32 * mb, 16 * (s + 1));
+          }
+          __builtin_amdgcn_sched_barrier(0);
           sAcc[mb] = mfma32(aq, kB[s], sAcc[mb]);
-          const bf16x8 ad = frag_row_s<C::NCH_D>(sdO, C::QW * wq + 32 * mb, 16 * s);
           pAcc[mb] = mfma32(ad, vB[s], pAcc[mb]);
+          __builtin_amdgcn_sched_barrier(0);
+          aq = aqn;
+          ad = adn;
         }
       };
       auto elem = [&](int mb) {
@@ -314,15 +326,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
         }
       };
       auto dvdk = [&](int mb) {
+        bf16x8 bo = frag_tr_s<C::NCH_D>(sdO, C::QW * wq + 16 * (2 * mb), 0, true);
+        bf16x8 bq = frag_tr_s<C::NCH_D>(sQ, C::QW * wq + 16 * (2 * mb), 0, true);
 #pragma unroll
-        for (int s = 2 * mb; s < 2 * mb + 2; ++s) {
-#pragma unroll
-          for (int n = 0; n < C::ND; ++n) {
-            const bf16x8 bo = frag_tr_s<C::NCH_D>(sdO, C::QW * wq + 16 * s, 32 * n, true);
-            dVacc[n] = mfma32(pB[s], bo, dVacc[n]);
-            const bf16x8 bq = frag_tr_s<C::NCH_D>(sQ, C::QW * wq + 16 * s, 32 * n, true);
-            dKacc[n] = mfma32(dsB[s], bq, dKacc[n]);
+        for (int x = 0; x < 2 * C::ND; ++x) {
+          const int s = 2 * mb + x / C::ND, n = x % C::ND;
+          bf16x8 bon = bo, bqn = bq;
+          if (x + 1 < 2 * C::ND) {
+            const int s1 = 2 * mb + (x + 1) / C::ND, n1 = (x + 1) % C::ND;
+            bon = frag_tr_s<C::NCH_D>(sdO, C::QW * wq + 16 * s1, 32 * n1, true);
+            bqn = frag_tr_s<C::NCH_D>(sQ, C::QW * wq + 16 * s1, 32 * n1, true);
           }
+          __builtin_amdgcn_sched_barrier(0);
+          dVacc[n] = mfma32(pB[s], bo, dVacc[n]);
+          dKacc[n] = mfma32(dsB[s], bq, dKacc[n]);
+          __builtin_amdgcn_sched_barrier(0);
+          bo = bon;
+          bq = bqn;
         }
       };
 
@@ -362,12 +382,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       f32x16 dqAcc[C::MQD];
 #pragma unroll
       for (int m = 0; m < C::MQD; ++m) dqAcc[m] = f32x16{};
+      {
+        bf16x8 ad[C::MQD];
 #pragma unroll
-      for (int s = 0; s < C::KKV; ++s) {
+        for (int m = 0; m < C::MQD; ++m) ad[m] = frag_tr_s<C::NCH_S>(sdS, 0, 32 * (mq0 + m), false);
 #pragma unroll
-        for (int m = 0; m < C::MQD; ++m) {
-          const bf16x8 ad = frag_tr_s<C::NCH_S>(sdS, 16 * s, 32 * (mq0 + m), false);
-          dqAcc[m] = mfma32(ad, kTB[s], dqAcc[m]);
+        for (int s = 0; s < C::KKV; ++s) {
+          bf16x8 adn[C::MQD];
+#pragma unroll
+          for (int m = 0; m < C::MQD; ++m)
+            adn[m] = s + 1 < C::KKV ? frag_tr_s<C::NCH_S>(sdS, 16 * (s + 1), 32 * (mq0 + m), false) : ad[m];
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int m = 0; m < C::MQD; ++m) dqAcc[m] = mfma32(ad[m], kTB[s], dqAcc[m]);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int m = 0; m < C::MQD; ++m) ad[m] = adn[m];
         }
       }
       trace_rec(2, t, gidx);
