@@ -67,7 +67,8 @@ def kernel_source_hash():
     import hashlib
 
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "deterministic_attention_backward_fa_amd", "csrc", "*")))
+    csrc = os.path.join(ROOT, "deterministic_attention_backward_fa_amd", "csrc")
+    files = sorted(f for ext in ("*.h", "*.hip", "*.cpp") for f in glob.glob(os.path.join(csrc, ext)))
     files.append(os.path.join(ROOT, "include", "detattn.h"))
     for f in files:
         h.update(os.path.basename(f).encode())

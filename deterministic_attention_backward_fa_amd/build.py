@@ -19,6 +19,9 @@ LIB = os.path.join(PKG, "libdetattn.so")
 ARCH = "gfx950"
 
 SOURCES = ["capi.cpp", "kernels_misc.hip", "bwd_d64.hip", "bwd_d128.hip"]
+# The main backward kernel keeps MFMA results the VALU reads in VGPRs (its
+# AGPR-resident accumulations are written as explicit AGPR-form MFMAs).
+PER_SOURCE = {"bwd_d64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "bwd_d128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 instructions.
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
@@ -34,7 +37,7 @@ def hipcc() -> str:
 
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), "-c", "-x", "hip", os.path.join(CSRC, src), "-o", obj] + COMMON + list(extra)
+    cmd = [hipcc(), "-c", "-x", "hip", os.path.join(CSRC, src), "-o", obj] + COMMON + PER_SOURCE.get(src, []) + list(extra)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

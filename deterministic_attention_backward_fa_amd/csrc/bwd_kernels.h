@@ -32,8 +32,8 @@ struct BwdArgs {
   const __bf16* k;
   const __bf16* v;
   const __bf16* dout;
-  const float* lse2;   // LSE * log2(e) per row
-  const float* delta;
+  const float* nlse;   // -LSE / scale per row (initial value of the S accumulator)
+  const float* ndelta; // -D per row (initial value of the dP accumulator)
   float* dqacc;
   __bf16* dk;
   __bf16* dv;
@@ -67,16 +67,17 @@ __device__ __forceinline__ unsigned hash3(unsigned a, unsigned b, unsigned c) {
 __device__ __forceinline__ long long now_ticks() { return (long long)__builtin_amdgcn_s_memrealtime(); }
 
 // ---------------------------------------------------------------------------
-// Preprocess: D_i = sum_d dO[i,d] * O[i,d] (fp32, fixed order), LSE_i in log2
-// units for the main kernel's exp2, zero the flags, the ticket and the error
-// word, and (unordered mode) the dQ accumulator.
+// Preprocess: D_i = sum_d dO[i,d] * O[i,d] (fp32, fixed order); the main
+// kernel's accumulator initial values -D_i and -LSE_i / scale; zero the flags,
+// the ticket and the error word, and (unordered mode) the dQ accumulator.
 // 16 threads per row, each summing 8 contiguous products in order, then a
 // fixed butterfly across the 16 lanes.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dout,
-                                                      const float* __restrict__ lse, float* __restrict__ lse2,
-                                                      float* __restrict__ delta, long long rows, int* flags,
+                                                      const float* __restrict__ lse, float inv_scale,
+                                                      float* __restrict__ nlse, float* __restrict__ ndelta,
+                                                      long long rows, int* flags,
                                                       long long n_flags, unsigned* header, float* dqacc,
                                                       long long dqacc_n4) {
   constexpr int TPR = D / 8;  // threads per row
@@ -95,8 +96,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
 #pragma unroll
   for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, TPR);
   if (row < rows && part == 0) {
-    delta[row] = acc;
-    lse2[row] = lse[row] * kLog2e;
+    ndelta[row] = -acc;
+    nlse[row] = -lse[row] * inv_scale;
   }
   for (long long f = gtid; f < n_flags; f += gsz) flags[f * kFlagInts] = 0;
   if (gtid < 64) header[gtid] = 0;

@@ -18,17 +18,32 @@
 // tile_sched.h decide the order). dQ = scale * accumulator is rounded to bf16
 // by the convert kernel; dK is scaled in the epilogue.
 //
-// Pipeline per tile t (buffer b = t & 1):
-//   top:  wait for this tile's LDS-DMA data and the previous tile's dQ adds,
-//         barrier, publish the previous tile's flag, start the DMA of tile t+1
-//         (Q, dO, LSE, D) into buffer b^1;
-//   S, dP, P, dS; dS^T -> LDS; barrier; dQ partial (MFMA);
-//   each wave waits (one lane polling) for the tile's flag, then issues its
-//   adds (fp32 atomic adds, or sc1 stores for the first contributor);
-//   dV, dK MFMAs run while those adds are in flight.
-// The accumulator is touched only through agent-scope coherent accesses, so
-// the hand-off needs no cache writeback or invalidate: "all adds done" is
-// vmcnt 0 in every wave before the barrier that precedes the flag store.
+// Accumulator initial values carry the row terms: the S accumulator of row q
+// starts at -LSE_q/scale (so P = exp2(scale*log2e * acc)) and the dP
+// accumulator at -D_q (so dS = P * acc). Causal masking sets the S initial
+// value to -inf above the diagonal, on diagonal tiles only.
+//
+// Instruction stream of one tile (one wave runs per SIMD, so MFMA, VALU and
+// LDS work overlap only when interleaved in the wave's own stream):
+//   top:   wait for this tile's LDS-DMA data and the previous tile's dQ adds,
+//          barrier, publish the previous tile's flag, DMA tile t+1 into the
+//          other buffer;
+//   A:     MFMA stream S/dP of row block 0, S/dP of block 1 (+ elementwise of
+//          block 0 between its MFMAs), dV/dK of block 0 (+ elementwise of
+//          block 1), ..., with the dS^T stores to LDS among the elementwise
+//          work; every MFMA's LDS operand is loaded PF MFMAs ahead;
+//   barrier (dS^T complete);
+//   B:     dQ partial MFMAs; wait for the dQ tile's turn; read the
+//          accumulator; dV/dK MFMAs of the last row block, with the
+//          accumulator adds placed among them.
+// The accumulator is touched only through coherent accesses (agent scope, or
+// workgroup scope when a ring of workgroups shares one XCD's L2), so the
+// hand-off needs no cache writeback: "all adds done" is vmcnt 0 in every wave
+// before the barrier that precedes the flag store.
+//
+// LDS tiles are row-major with 16 bytes of padding per row: 16 consecutive
+// rows read at one column start on 16 different 4-bank groups, and every
+// fragment address is one per-lane register plus a compile-time offset.
 #pragma once
 #include "common.h"
 #include "tile_sched.h"
@@ -49,22 +64,31 @@ struct MainCfg {
   static constexpr int KKV = BKV / 16;   // MFMA K steps over the KV tile
   static constexpr int WPD = 4 / ND;     // waves per D block of the dQ tile
   static constexpr int MQD = (BQ / 32) / WPD;
-  static constexpr int NCH_D = D / 8;    // 16-byte chunks per Q/dO/K/V row
-  static constexpr int NCH_S = BQ / 8;   // 16-byte chunks per dS^T row
-  static constexpr int Q_BYTES = BQ * D * 2;
-  static constexpr int K_BYTES = BKV * D * 2;
-  static constexpr int S_BYTES = BKV * BQ * 2;
-  static constexpr int LD_BYTES = BQ * 4 * 2;  // LSE then D
-  static constexpr int OFF_Q0 = 0;
-  static constexpr int OFF_Q1 = OFF_Q0 + Q_BYTES;
-  static constexpr int OFF_DO0 = OFF_Q1 + Q_BYTES;
-  static constexpr int OFF_DO1 = OFF_DO0 + Q_BYTES;
-  static constexpr int OFF_LD0 = OFF_DO1 + Q_BYTES;
-  static constexpr int OFF_LD1 = OFF_LD0 + LD_BYTES;
-  static constexpr int OFF_DS = OFF_LD1 + LD_BYTES;
-  static constexpr int OFF_K = OFF_DS + S_BYTES;
-  static constexpr int OFF_V = OFF_K + K_BYTES;
-  static constexpr int TILE_END = OFF_V + K_BYTES;
+  static constexpr int NCH = D / 8;      // 16-byte chunks per Q/dO/K/V row
+  static constexpr int PD = D * 2 + 16;  // padded row pitch of Q/dO/K/V tiles (bytes)
+  static constexpr int PS = BQ * 2 + 16; // padded row pitch of the dS^T tile (bytes)
+  static constexpr int QB = BQ * PD;     // one Q or dO tile
+  static constexpr int KB = BKV * PD;    // one K or V tile
+  static constexpr int SB = BKV * PS;    // dS^T tile (row kv, column q)
+  static constexpr int LDB = BQ * 8;     // -LSE/scale then -D, fp32
+  static constexpr int BUF = 2 * QB + LDB;  // one Q-tile buffer: Q, dO, row terms
+  static constexpr int OFF_DS = 0;
+  static constexpr int OFF_B0 = SB;      // buffer b (0..2) at OFF_B0 + b * BUF
+  // K_j, V_j are staged in buffers 1-2 at the start of a column (they move to
+  // registers before those buffers receive Q tiles)
+  static constexpr int OFF_K = OFF_B0 + BUF;
+  static constexpr int OFF_V = OFF_K + KB;
+  static constexpr int TILE_END = OFF_B0 + 3 * BUF;
+  static constexpr int DMA_Q = BQ * (NCH + 1) / 64;  // 1 KB DMA instructions per padded Q/dO tile
+  static constexpr int DMA_K = BKV * (NCH + 1) / 64;
+  static constexpr int DMA_QW = (DMA_Q + 3) / 4;     // per wave, at most
+  // vector-memory instructions one wave issues for one Q tile (Q and dO rows,
+  // plus the row terms on waves 0 and 1)
+  static constexpr int dma_ops(int w) {
+    int n = 0;
+    for (int x = w; x < DMA_Q; x += 4) n += 2;
+    return n + (w < 2 ? BQ / 64 : 0);
+  }
   // Epilogue scratch, aliasing the tile buffers (nothing is in flight then):
   // per output tensor, the fp32 partials of the waves with wq == 1 (NQW == 2)
   // and a padded bf16 tile for coalesced stores.
@@ -76,9 +100,171 @@ struct MainCfg {
   static constexpr int LDS_BYTES = OFF_MISC + 16;
   static_assert(NKVW * NQW == 4, "4 waves");
   static_assert(QW % 32 == 0 && MQD >= 1, "tile shape");
-  static_assert((BQ * D / 8) % 256 == 0 && (BKV * D / 8) % 256 == 0, "DMA granularity");
+  static_assert((BQ * (NCH + 1)) % 64 == 0 && (BKV * (NCH + 1)) % 64 == 0, "DMA granularity");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(OFF_V + KB <= TILE_END, "K, V staging");
+  static_assert(dma_ops(0) <= 63, "vmcnt field");
 };
+
+// Order of the MFMAs of stream A (before the dS^T barrier). Group gi holds the
+// S/dP MFMAs of row block gi (gi < MQ) followed by the dV/dK MFMAs of row block
+// gi - 2 (2 <= gi <= MQ); the elementwise work of block gi - 1 is spread over
+// group gi. Each MFMA is identified by kind (0 S, 1 dP, 2 dV, 3 dK), row block
+// and step (K step for S/dP; 0 .. 2*ND-1 over (Q K step, D block) for dV/dK).
+template <class C>
+struct StreamA {
+  static constexpr int NSDP = 2 * C::KD;
+  static constexpr int NDK = 4 * C::ND;
+  static constexpr int gsize(int gi) { return (gi < C::MQ ? NSDP : 0) + (gi >= 2 && gi <= C::MQ ? NDK : 0); }
+  static constexpr int gstart(int gi) {
+    int s = 0;
+    for (int x = 0; x < gi; ++x) s += gsize(x);
+    return s;
+  }
+  static constexpr int N = gstart(C::MQ + 1);
+  static constexpr int group(int k) {
+    int gi = 0;
+    while (gi < C::MQ && k >= gstart(gi + 1)) ++gi;
+    return gi;
+  }
+  static constexpr int rel(int k) { return k - gstart(group(k)); }
+  static constexpr bool sdp(int k) { return group(k) < C::MQ && rel(k) < NSDP; }
+  static constexpr int drel(int k) { return rel(k) - (group(k) < C::MQ ? NSDP : 0); }
+  static constexpr int kind(int k) { return sdp(k) ? (rel(k) & 1) : 2 + (drel(k) & 1); }
+  static constexpr int blk(int k) { return sdp(k) ? group(k) : group(k) - 2; }
+  static constexpr int step(int k) { return sdp(k) ? (rel(k) >> 1) : (drel(k) >> 1); }
+  // LDS instructions of MFMA k's operand load, and those issued after it by
+  // the time MFMA k runs (operands are loaded pf MFMAs ahead)
+  static constexpr int nloads(int k) { return sdp(k) ? 1 : 2; }
+  static constexpr int loads_after(int k, int pf) {
+    int n = 0;
+    for (int x = k + 1; x <= k + pf && x < N; ++x) n += nloads(x);
+    return n;
+  }
+  // elementwise units (16 elements + 4 dS^T stores) issued after the j-th MFMA
+  // of a group of size G: the first DELAY MFMAs of the group carry none, so
+  // the previous group's last results have landed.
+  static constexpr int kUnits = 20;
+  static constexpr int kDelay = 1;
+  static constexpr int units_before(int j, int G) {
+    return j <= kDelay ? 0 : (j >= G ? kUnits : ((j - kDelay) * kUnits) / (G - kDelay));
+  }
+};
+
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
+
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+#define DETATTN_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// LDS operand loads of the MFMA streams are issued from inline assembly and
+// waited for explicitly: the compiler would otherwise make every transposed
+// read wait for all LDS-DMA transfers in flight (the next tile's prefetch).
+// lgkm_wait<N> returns once at most N LDS operations are outstanding; the
+// streams pass the number of their own loads issued after the awaited one, so
+// any other LDS traffic can only make the wait longer, never too short. The
+// awaited register is tied to the wait so the consuming MFMA stays after it.
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_ld16_asm(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "DS offset field");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_tr_asm(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "DS offset field");
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_ld16_agpr(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "DS offset field");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=a"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_tr_agpr(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "DS offset field");
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=a"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+__device__ __forceinline__ void lgkm_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x4& x) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt field");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(N));
+}
+// the two halves of a transposed operand are tied to the wait before they are
+// combined, so no copy of either half can run ahead of the data
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x2& lo, u32x2& hi) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt field");
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(lo), "+v"(hi) : "i"(N));
+}
+template <int N, class T>
+__device__ __forceinline__ void lgkm_wait_agpr(T& x) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt field");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+a"(x) : "i"(N));
+}
+// one MFMA operand in flight: a 16-byte row read, or two transposed 8-byte reads
+struct Opnd {
+  u32x4 q;
+  u32x2 lo, hi;
+};
+__device__ __forceinline__ u32x4 cat2(const u32x2& a, const u32x2& b) { return u32x4{a[0], a[1], b[0], b[1]}; }
+
+// Workgroup barrier for LDS hand-offs only: LDS operations are complete, but
+// vector-memory loads in flight (the prefetch DMA) stay in flight.
+// (__syncthreads also waits for every outstanding vector-memory operation.)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// Wait until at most N vector-memory operations of this wave are in flight
+// (they complete in issue order), then barrier.
+template <int N>
+__device__ __forceinline__ void vm_barrier() {
+  static_assert(N >= 0 && N <= 63, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"i"(N) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& x) { return __builtin_bit_cast(bf16x8, x); }
+// keep a value in accumulation registers (AGPRs): MFMA-only operands live
+// there, which leaves the VGPRs to the values the VALU works on
+template <class T>
+__device__ __forceinline__ void pin_agpr(T& x) {
+  asm volatile("" : "+a"(x));
+}
+// dV/dK accumulation: an MFMA whose accumulator stays in AGPRs (the other
+// MFMAs of the kernel are compiled in VGPR form, so the VALU reads S, dP and
+// the dQ partial without copies). The compiler does not see these as MFMAs,
+// so their hazards are covered by construction: the A operand (P or dS,
+// written by the VALU) is produced at least one MFMA group earlier, the B
+// operand arrives through lgkm_wait, consecutive uses of one accumulator are
+// 2*ND - 1 MFMAs apart, and mfma_agpr_drain() runs before the VALU reads the
+// accumulators.
+__device__ __forceinline__ void mfma_agpr(f32x16& acc, const bf16x8& a, const u32x4& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// more wait states than an MFMA result needs before a VALU read
+__device__ __forceinline__ void mfma_agpr_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+// keep a value in VGPRs (accumulators the VALU reads)
+template <class T>
+__device__ __forceinline__ void pin_vgpr(T& x) {
+  asm volatile("" : "+v"(x));
+}
 
 // Epilogue of one KV tile: (NQW == 2) fold the wq == 1 waves' partial sums into
 // the wq == 0 waves, round to bf16 (times `mul`) through a padded LDS tile and
@@ -122,26 +308,44 @@ __device__ __forceinline__ void store_column(f32x16 (&acc)[C::ND], float mul, __
   __syncthreads();
 }
 
+// Global byte offset, inside a row-major tile of NCH-chunk rows, of the chunk
+// that lane `lane` of DMA instruction `ins` moves into the padded LDS tile
+// (NCH + 1 chunks per row). Padding chunks re-read chunk 0 of their row; those
+// bytes land in the padding and are never read.
+template <int NCH>
+__device__ __forceinline__ int dma_goff(int ins, int lane) {
+  const int p = ins * 64 + lane;
+  const int row = p / (NCH + 1), col = p % (NCH + 1);
+  return row * (NCH * 16) + (col < NCH ? col : 0) * 16;
+}
+
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds) {
+  __builtin_amdgcn_global_load_lds((gbl_void*)gsrc, (lds_void*)lds, 16, 0, 0);
+}
+
 template <int D, int BQ, int BKV, bool CAUSAL, int DQM>
 __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   using C = MainCfg<D, BQ, BKV>;
+  using SA = StreamA<C>;
+  constexpr int PF = 4;       // LDS operand loads run this many MFMAs ahead
+  constexpr int RING = PF + 2;  // operand registers; a slot is reloaded two MFMAs after its last reader
   // Scope of the accumulator accesses: across XCDs (sc1), or inside the XCD's
   // L2 (sc0) when every workgroup of a ring runs on one XCD. sc0 loads may hit
   // the compute unit's own L1, so that mode invalidates L1 (buffer_inv sc0)
   // after observing the flag and before loading. Flags always use sc1.
   constexpr int kScope = DQM == kDqLocalRmw ? __HIP_MEMORY_SCOPE_WORKGROUP : __HIP_MEMORY_SCOPE_AGENT;
   constexpr int kFlagScope = __HIP_MEMORY_SCOPE_AGENT;
+  constexpr bool kRmw = DQM == kDqOrderedRmw || DQM == kDqLocalRmw;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  __bf16* sK = reinterpret_cast<__bf16*>(smem + C::OFF_K);
-  __bf16* sV = reinterpret_cast<__bf16*>(smem + C::OFF_V);
-  __bf16* sdS = reinterpret_cast<__bf16*>(smem + C::OFF_DS);
   int* sMisc = reinterpret_cast<int*>(smem + C::OFF_MISC);
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 5;
   const int c32 = lane & 31;
+  const int s16 = lane & 15;
+  const int grp = lane >> 4;
   const int wk = w % C::NKVW;
   const int wq = w / C::NKVW;
   const int nbq = w % C::ND;             // dQ: this wave's D block
@@ -150,6 +354,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   const Sched sc = a.sc;
   const int ipH = sc.items_per_head();
   const long long total_items = (long long)a.BH * ipH;
+
+  // Per-lane LDS byte offsets; everything else in a fragment address is a
+  // compile-time offset (or the per-tile buffer base).
+  const int trcol = (16 * (grp & 1) + 4 * (s16 & 3)) * 2;
+  const int oA = (C::QW * wq + c32) * C::PD + g * 16;                // Q/dO row fragments (buffer-relative)
+  const int oT = (C::QW * wq + 4 * g + (s16 >> 2)) * C::PD + trcol;  // Q/dO transposed fragments, accumulator K order
+  const int oS = C::OFF_DS + (8 * g + (s16 >> 2)) * C::PS + trcol + 64 * mq0;     // dS transposed fragments
+  const int oW = C::OFF_DS + (32 * wk + c32) * C::PS + (C::QW * wq + 4 * g) * 2;  // dS^T stores
+  const int oL = 2 * C::QB + (C::QW * wq + 4 * g) * 4;                            // row terms (buffer-relative)
+  const int dqlane = ((32 * mq0 + 4 * g) * D + 32 * nbq + c32) * 4;  // dQ accumulator tile, per lane
+  int goffQ[C::DMA_QW];
+#pragma unroll
+  for (int x = 0; x < C::DMA_QW; ++x) goffQ[x] = dma_goff<C::NCH>(w + 4 * x, lane);
 
   int ring_id = 0, slot = 0;
   if (!a.ticket_mode) {
@@ -172,16 +389,29 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     }
   }
 
-  // Q, dO, LSE and D of Q tile i -> buffer b (asynchronous).
+  auto ld16 = [&](int off) -> bf16x8 { return *reinterpret_cast<const bf16x8*>(smem + off); };
+  const uint32_t lbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)smem;
+  const uint32_t aS = lbase + oS;
+  auto ldtr = [&](int off) -> bf16x4 { return lds_read_tr(reinterpret_cast<const __bf16*>(smem + off)); };
+
+  // Q, dO and the row terms of Q tile i -> buffer b (asynchronous).
   auto dma_q = [&](int b, long long head_off, long long bhS, int i) {
     const long long qrow0 = (long long)i * BQ;
-    __bf16* dq_ = reinterpret_cast<__bf16*>(smem + (b ? C::OFF_Q1 : C::OFF_Q0));
-    __bf16* ddo = reinterpret_cast<__bf16*>(smem + (b ? C::OFF_DO1 : C::OFF_DO0));
-    float* ld = reinterpret_cast<float*>(smem + (b ? C::OFF_LD1 : C::OFF_LD0));
-    dma_tile<C::NCH_D>(dq_, a.q + head_off + qrow0 * D, BQ);
-    dma_tile<C::NCH_D>(ddo, a.dout + head_off + qrow0 * D, BQ);
-    dma_f32(ld, a.lse2 + bhS + qrow0, BQ, 0);
-    dma_f32(ld + BQ, a.delta + bhS + qrow0, BQ, 1);
+    unsigned char* base = smem + C::OFF_B0 + b * C::BUF;
+    const unsigned char* gq = reinterpret_cast<const unsigned char*>(a.q + head_off + qrow0 * D);
+    const unsigned char* gd = reinterpret_cast<const unsigned char*>(a.dout + head_off + qrow0 * D);
+    // goffQ[x] < 2^31: tile-relative byte offsets (uniform base + 32-bit offset addressing)
+#pragma unroll
+    for (int x = 0; x < C::DMA_QW; ++x) {
+      const int ins = w + 4 * x;
+      if (ins < C::DMA_Q) {
+        dma16(gq + (uint32_t)goffQ[x], base + ins * 1024);
+        dma16(gd + (uint32_t)goffQ[x], base + C::QB + ins * 1024);
+      }
+    }
+    float* ld = reinterpret_cast<float*>(base + 2 * C::QB);
+    dma_f32(ld, a.nlse + bhS + qrow0, BQ, 0);
+    dma_f32(ld + BQ, a.ndelta + bhS + qrow0, BQ, 1);
   };
 
   // Optional phase trace: wave 0, lane 0 of each workgroup.
@@ -200,7 +430,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     if (a.ticket_mode) {
       if (tid == 0) sMisc[0] = (int)atomicAdd(a.ticket, 1u);
       __syncthreads();
-      gidx = sMisc[0];
+      gidx = __builtin_amdgcn_readfirstlane(sMisc[0]);
       __syncthreads();
       if (gidx >= total_items) return;
     } else {
@@ -210,7 +440,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     }
     const int bh = (int)(gidx / ipH);
     const int it = (int)(gidx % ipH);
-    const int len = sc.item_len(it);
     const long long head_off = (long long)bh * a.S * D;
     const long long bhS = (long long)bh * a.S;
 
@@ -222,198 +451,273 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     int i0, j;
     sc.tile(it, t_begin, i0, j);
     // ---- segment prologue: K_j, V_j and the first Q tile, synchronously ----
-    dma_tile<C::NCH_D>(sK, a.k + head_off + (long long)j * BKV * D, BKV);
-    dma_tile<C::NCH_D>(sV, a.v + head_off + (long long)j * BKV * D, BKV);
+    {
+      const unsigned char* gk = reinterpret_cast<const unsigned char*>(a.k + head_off + (long long)j * BKV * D);
+      const unsigned char* gv = reinterpret_cast<const unsigned char*>(a.v + head_off + (long long)j * BKV * D);
+      for (int ins = w; ins < C::DMA_K; ins += 4) {
+        const int go = dma_goff<C::NCH>(ins, lane);
+        dma16(gk + go, smem + C::OFF_K + ins * 1024);
+        dma16(gv + go, smem + C::OFF_V + ins * 1024);
+      }
+    }
     dma_q(0, head_off, bhS, i0);
     wait_vm_all();
     __syncthreads();
+    // K_j, V_j (MFMA B operands of S, dP) and K_j transposed (B operand of the
+    // dQ partial) go straight into AGPRs
     bf16x8 kB[C::KD], vB[C::KD], kTB[C::KKV];
+    {
+      const uint32_t ak = lbase + C::OFF_K + (32 * wk + c32) * C::PD + g * 16;
+      const uint32_t av = ak + (C::OFF_V - C::OFF_K);
+      const uint32_t akt = lbase + C::OFF_K + (8 * g + (s16 >> 2)) * C::PD + trcol + 64 * nbq;
+      u32x4 kq[C::KD], vq[C::KD];
+      u32x2 tlo[C::KKV], thi[C::KKV];
+      static_for<0, C::KD>([&](auto sc_) {
+        constexpr int s = decltype(sc_)::value;
+        kq[s] = lds_ld16_agpr<32 * s>(ak);
+        vq[s] = lds_ld16_agpr<32 * s>(av);
+      });
+      static_for<0, C::KKV>([&](auto sc_) {
+        constexpr int s = decltype(sc_)::value;
+        tlo[s] = lds_tr_agpr<16 * s * C::PD>(akt);
+        thi[s] = lds_tr_agpr<(16 * s + 4) * C::PD>(akt);
+      });
+      // every loaded register is tied to a wait that covers it (loads complete in order)
+      static_for<0, C::KD>([&](auto sc_) {
+        constexpr int s = decltype(sc_)::value;
+        constexpr int after_k = 2 * (C::KD - 1 - s) + 1 + 2 * C::KKV;
+        lgkm_wait_agpr<cmin(after_k, 15)>(kq[s]);  // more loads than the counter holds: 15 is still safe
+        lgkm_wait_agpr<cmin(after_k - 1, 15)>(vq[s]);
+      });
+      static_for<0, C::KKV>([&](auto sc_) {
+        constexpr int s = decltype(sc_)::value;
+        constexpr int after_t = 2 * (C::KKV - 1 - s);
+        lgkm_wait_agpr<cmin(after_t + 1, 15)>(tlo[s]);
+        lgkm_wait_agpr<cmin(after_t, 15)>(thi[s]);
+      });
 #pragma unroll
-    for (int s = 0; s < C::KD; ++s) {
-      kB[s] = frag_row_s<C::NCH_D>(sK, 32 * wk, 16 * s);
-      vB[s] = frag_row_s<C::NCH_D>(sV, 32 * wk, 16 * s);
+      for (int s = 0; s < C::KD; ++s) {
+        kB[s] = as_bf16x8(kq[s]);
+        vB[s] = as_bf16x8(vq[s]);
+        pin_agpr(kB[s]);
+        pin_agpr(vB[s]);
+      }
+#pragma unroll
+      for (int s = 0; s < C::KKV; ++s) {
+        kTB[s] = as_bf16x8(cat2(tlo[s], thi[s]));
+        pin_agpr(kTB[s]);
+      }
     }
-#pragma unroll
-    for (int s = 0; s < C::KKV; ++s) kTB[s] = frag_tr_s<C::NCH_D>(sK, 16 * s, 32 * nbq, false);
+    // K, V are in registers: buffers 1-2 are free for the next Q tiles
+    lds_barrier();
+    bool dma_pending = t_begin + 1 < t_end;  // this wave's newest vector-memory ops are a tile's DMA
+    if (dma_pending) {
+      int ni, nj;
+      sc.tile(it, t_begin + 1, ni, nj);
+      dma_q(1, head_off, bhS, ni);
+    }
     f32x16 dKacc[C::ND], dVacc[C::ND];
 #pragma unroll
     for (int n = 0; n < C::ND; ++n) {
       dKacc[n] = f32x16{};
       dVacc[n] = f32x16{};
+      pin_agpr(dKacc[n]);
+      pin_agpr(dVacc[n]);
     }
     trace_rec(6, t_begin, gidx);
 
     int t = t_begin;
+    int b = 0;  // buffer of tile t
     do {
       int i, jj;
       sc.tile(it, t, i, jj);
-      const int b = (t - t_begin) & 1;
       const long long qrow0 = (long long)i * BQ;
       trace_rec(0, t, gidx);
-      // prefetch the next tile of this column into the other buffer
-      if (t + 1 < t_end) {
-        int ni, nj;
-        sc.tile(it, t + 1, ni, nj);
-        dma_q(b ^ 1, head_off, bhS, ni);
-      }
-      const __bf16* sQ = reinterpret_cast<const __bf16*>(smem + (b ? C::OFF_Q1 : C::OFF_Q0));
-      const __bf16* sdO = reinterpret_cast<const __bf16*>(smem + (b ? C::OFF_DO1 : C::OFF_DO0));
-      const float* sL = reinterpret_cast<const float*>(smem + (b ? C::OFF_LD1 : C::OFF_LD0));
-      const float* sDl = sL + BQ;
-
-      // Per 32-row block mb of this wave's Q rows the work is: S and dP
-      // (2*KD MFMAs), the elementwise P/dS (VALU), and dV/dK over the block's
-      // two K steps (4*ND MFMAs). Blocks are pipelined so that the MFMAs of one
-      // block run while the VALU of the previous one executes; the last
-      // block's dV/dK is deferred until after the dQ hand-off, where it covers
-      // the latency of the accumulator adds.
-      const bool diag = CAUSAL && ((long long)(j + 1) * BKV - 1 > qrow0);
-      // kv - q offset of this lane's column against the tile's first Q row;
-      // pushed far below any q when the tile needs no mask (branch-free).
-      const int kv_rel = diag ? (int)((long long)j * BKV - qrow0) + 32 * wk + c32 : -(1 << 30);
-      f32x16 sAcc[C::MQ], pAcc[C::MQ];
-      bf16x8 pB[C::KQ], dsB[C::KQ];
-
-      // Operand fragments are software-pipelined one K step ahead: the loads
-      // of step s+1 are issued before the MFMAs of step s (sched_barrier keeps
-      // the compiler from regrouping them), so LDS latency overlaps the MFMAs.
-      auto sdp = [&](int mb) {
-        sAcc[mb] = f32x16{};
-        pAcc[mb] = f32x16{};
-        bf16x8 aq = frag_row_s<C::NCH_D>(sQ, C::QW * wq + 32 * mb, 0);
-        bf16x8 ad = frag_row_s<C::NCH_D>(sdO, C::QW * wq + 32 * mb, 0);
-#pragma unroll
-        for (int s = 0; s < C::KD; ++s) {
-          bf16x8 aqn = aq, adn = ad;
-          if (s + 1 < C::KD) {
-            aqn = frag_row_s<C::NCH_D>(sQ, C::QW * wq + 32 * mb, 16 * (s + 1));
-            adn = frag_row_s<C::NCH_D>(sdO, C::QW * wq + 32 * mb, 16 * (s + 1));
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          sAcc[mb] = mfma32(aq, kB[s], sAcc[mb]);
-          pAcc[mb] = mfma32(ad, vB[s], pAcc[mb]);
-          __builtin_amdgcn_sched_barrier(0);
-          aq = aqn;
-          ad = adn;
-        }
-      };
-      auto elem = [&](int mb) {
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int qloc = C::QW * wq + 32 * mb + 8 * rq + 4 * g;
-          const f32x4 L4 = *reinterpret_cast<const f32x4*>(sL + qloc);
-          const f32x4 D4 = *reinterpret_cast<const f32x4*>(sDl + qloc);
-          float p[4], ds[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * rq + e;
-            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sAcc[mb][r], c1, -L4[e]));
-            p[e] = kv_rel > qloc + e ? 0.f : p[e];
-            ds[e] = p[e] * (pAcc[mb][r] - D4[e]);
-          }
-          const int kstep = 2 * mb + (rq >> 1);
-          const int sl = 4 * (rq & 1);
-          const bf16x2 p01 = cvt2(p[0], p[1]), p23 = cvt2(p[2], p[3]);
-          const bf16x2 d01 = cvt2(ds[0], ds[1]), d23 = cvt2(ds[2], ds[3]);
-          pB[kstep][sl] = p01[0];
-          pB[kstep][sl + 1] = p01[1];
-          pB[kstep][sl + 2] = p23[0];
-          pB[kstep][sl + 3] = p23[1];
-          dsB[kstep][sl] = d01[0];
-          dsB[kstep][sl + 1] = d01[1];
-          dsB[kstep][sl + 2] = d23[0];
-          dsB[kstep][sl + 3] = d23[1];
-        }
-      };
-      auto dvdk = [&](int mb) {
-        bf16x8 bo = frag_tr_s<C::NCH_D>(sdO, C::QW * wq + 16 * (2 * mb), 0, true);
-        bf16x8 bq = frag_tr_s<C::NCH_D>(sQ, C::QW * wq + 16 * (2 * mb), 0, true);
-#pragma unroll
-        for (int x = 0; x < 2 * C::ND; ++x) {
-          const int s = 2 * mb + x / C::ND, n = x % C::ND;
-          bf16x8 bon = bo, bqn = bq;
-          if (x + 1 < 2 * C::ND) {
-            const int s1 = 2 * mb + (x + 1) / C::ND, n1 = (x + 1) % C::ND;
-            bon = frag_tr_s<C::NCH_D>(sdO, C::QW * wq + 16 * s1, 32 * n1, true);
-            bqn = frag_tr_s<C::NCH_D>(sQ, C::QW * wq + 16 * s1, 32 * n1, true);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          dVacc[n] = mfma32(pB[s], bo, dVacc[n]);
-          dKacc[n] = mfma32(dsB[s], bq, dKacc[n]);
-          __builtin_amdgcn_sched_barrier(0);
-          bo = bon;
-          bq = bqn;
-        }
-      };
-
-      sdp(0);
-#pragma unroll
-      for (int mb = 1; mb < C::MQ; ++mb) {
-        sdp(mb);
-        elem(mb - 1);
-        if (mb >= 2) dvdk(mb - 2);
-      }
-      elem(C::MQ - 1);
-      if (C::MQ >= 2) dvdk(C::MQ - 2);
-
-      // ---- dS^T -> LDS (row kv, column q), 4 consecutive q per 8-byte store ----
-#pragma unroll
-      for (int s = 0; s < C::KQ; ++s) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int q0 = C::QW * wq + 16 * s + 8 * hh + 4 * g;
-          bf16x4 v4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = dsB[s][4 * hh + e];
-          *reinterpret_cast<bf16x4*>(sdS + swz_off<C::NCH_S>(32 * wk + c32, q0)) = v4;
-        }
-      }
-      trace_rec(1, t, gidx);
-
-      // The dQ tile's flag is read now; the load completes under the barrier
-      // and the dQ MFMAs, and is only re-polled if the turn has not come yet.
+      // this tile's turn in dQ tile i's order: rank rk, flag = number of adds done
       const int rk = DQM == kDqUnordered ? 0 : sc.rank(i, j);
       int* flag = a.flags + ((long long)bh * sc.n_q + i) * kFlagInts;
+      const int vb = C::OFF_B0 + b * C::BUF;
+      const int vL = oL + vb;
+      const uint32_t aA = lbase + oA + vb, aT = lbase + oT + vb;
+
+      // ---- accumulator initial values: -LSE/scale (S), -D (dP); mask on diagonal tiles ----
+      f32x16 sAcc[C::MQ], pAcc[C::MQ];
+#pragma unroll
+      for (int m = 0; m < C::MQ; ++m)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(smem + vL + (32 * m + 8 * rq) * 4);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(smem + vL + BQ * 4 + (32 * m + 8 * rq) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sAcc[m][4 * rq + e] = l4[e];
+            pAcc[m][4 * rq + e] = d4[e];
+          }
+        }
+#pragma unroll
+      for (int m = 0; m < C::MQ; ++m) {
+        pin_vgpr(sAcc[m]);
+        pin_vgpr(pAcc[m]);
+      }
+      if (CAUSAL && (long long)(j + 1) * BKV - 1 > qrow0) {
+        // key index minus query index, both relative to the tile's first Q row
+        const int kv_rel = (int)((long long)j * BKV - qrow0) + 32 * wk + c32 - C::QW * wq - 4 * g;
+#pragma unroll
+        for (int m = 0; m < C::MQ; ++m)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kv_rel > 32 * m + 8 * (r >> 2) + (r & 3)) sAcc[m][r] = -__builtin_inff();
+      }
+
+      bf16x8 pB[C::KQ], dsB[C::KQ];
+      float pv[16], dv[16];
+      Opnd ring[RING];
+
+      // LDS operand of stream-A MFMA k (S, dP: one row read; dV, dK: two transposed reads)
+      auto loadA = [&](auto kc, Opnd& o) {
+        constexpr int k = decltype(kc)::value;
+        constexpr int kind = SA::kind(k), m = SA::blk(k), st = SA::step(k);
+        if constexpr (kind == 0) o.q = lds_ld16_asm<32 * m * C::PD + 32 * st>(aA);
+        else if constexpr (kind == 1) o.q = lds_ld16_asm<C::QB + 32 * m * C::PD + 32 * st>(aA);
+        else {
+          constexpr int sq = 2 * m + st / C::ND, n = st % C::ND;
+          constexpr int off = (kind == 2 ? C::QB : 0) + 16 * sq * C::PD + 64 * n;
+          o.lo = lds_tr_asm<off>(aT);
+          o.hi = lds_tr_asm<off + 8 * C::PD>(aT);
+        }
+      };
+      // wait for MFMA k's operand (N = own loads issued after it) and return it
+      auto waitA = [&](auto kc, Opnd& o) -> u32x4 {
+        constexpr int k = decltype(kc)::value;
+        constexpr int N = SA::loads_after(k, PF);
+        if constexpr (SA::sdp(k)) {
+          lgkm_wait<N>(o.q);
+          return o.q;
+        } else {
+          lgkm_wait<N>(o.lo, o.hi);
+          return cat2(o.lo, o.hi);
+        }
+      };
+      auto mfmaA = [&](auto kc, const u32x4& opr) {
+        constexpr int k = decltype(kc)::value;
+        constexpr int kind = SA::kind(k), m = SA::blk(k), st = SA::step(k);
+        const bf16x8 op = as_bf16x8(opr);
+        if constexpr (kind == 0) sAcc[m] = mfma32(op, kB[st], sAcc[m]);
+        else if constexpr (kind == 1) pAcc[m] = mfma32(op, vB[st], pAcc[m]);
+        else {
+          constexpr int sq = 2 * m + st / C::ND, n = st % C::ND;
+          if constexpr (kind == 2) mfma_agpr(dVacc[n], pB[sq], opr);
+          else mfma_agpr(dKacc[n], dsB[sq], opr);
+        }
+      };
+      // elementwise unit u of row block e: 4 elements then one dS^T store, x4
+      auto unitA = [&](auto ec, auto uc) {
+        constexpr int e = decltype(ec)::value, u = decltype(uc)::value;
+        constexpr int q4 = u / 5, pos = u % 5;
+        if constexpr (pos < 4) {
+          constexpr int r = 4 * q4 + pos;
+          pv[r] = __builtin_amdgcn_exp2f(c1 * sAcc[e][r]);
+          dv[r] = pv[r] * pAcc[e][r];
+          if constexpr (r & 1) {
+            constexpr int sq = 2 * e + (r >> 3), sl = (r - 1) & 7;
+            const bf16x2 p2 = cvt2(pv[r - 1], pv[r]);
+            const bf16x2 d2 = cvt2(dv[r - 1], dv[r]);
+            pB[sq][sl] = p2[0];
+            pB[sq][sl + 1] = p2[1];
+            dsB[sq][sl] = d2[0];
+            dsB[sq][sl + 1] = d2[1];
+          }
+        } else {
+          // rows 4*q4 .. 4*q4+3 of the block: Q K step 2e + q4/2, half q4 & 1
+          constexpr int sq = 2 * e + (q4 >> 1), hh = q4 & 1;
+          bf16x4 v4;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) v4[x] = dsB[sq][4 * hh + x];
+          *reinterpret_cast<bf16x4*>(smem + oW + (16 * sq + 8 * hh) * 2) = v4;
+        }
+      };
+
+      // ---- stream A ----
+      static_for<0, PF>([&](auto kc) {
+        if constexpr (decltype(kc)::value < SA::N) loadA(kc, ring[decltype(kc)::value]);
+      });
+      static_for<0, SA::N>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        if constexpr (k + PF < SA::N) loadA(std::integral_constant<int, k + PF>{}, ring[(k + PF) % RING]);
+        mfmaA(kc, waitA(kc, ring[k % RING]));
+        DETATTN_FENCE();
+        constexpr int gi = SA::group(k);
+        if constexpr (gi >= 1) {
+          constexpr int G = SA::gsize(gi), jx = k - SA::gstart(gi);
+          constexpr int u0 = SA::units_before(jx, G), u1 = SA::units_before(jx + 1, G);
+          static_for<u0, u1>([&](auto uc) { unitA(std::integral_constant<int, gi - 1>{}, uc); });
+        }
+        DETATTN_FENCE();
+      });
+      if constexpr (SA::gsize(C::MQ) == 0)  // one row block: its elementwise work has no MFMAs to hide under
+        static_for<0, SA::kUnits>([&](auto uc) { unitA(std::integral_constant<int, C::MQ - 1>{}, uc); });
+      trace_rec(1, t, gidx);
+
+      // The dQ tile's flag is read now; the load completes under the barrier,
+      // and the flag is re-polled after the dQ MFMAs only if the turn has not come.
       int seen = rk;
       if (DQM != kDqUnordered && rk > 0 && lane == 0) seen = __hip_atomic_load(flag, __ATOMIC_RELAXED, kFlagScope);
-      __syncthreads();
+      lds_barrier();  // dS^T complete
+      // early: the turn has come already (or this is the first contribution),
+      // so the accumulator is read right away and the adds are issued early;
+      // the delay injection of the tests always takes the late path
+      const bool early = DQM != kDqUnordered &&
+                         (rk == 0 || (a.delay_seed == 0 && __builtin_amdgcn_readfirstlane(seen) == rk));
 
-      // ---- dQ partial = dS K (this wave's D block, MQD row blocks) ----
+      // ---- stream B: dQ partial = dS K (this wave's D block, MQD row blocks), then dV/dK of the last block ----
+      constexpr int NB1 = C::MQD * C::KKV;
+      constexpr int NB = NB1 + SA::NDK;
+      // MFMA index before which the RMW adds are issued: early when the reads
+      // went out before the dQ MFMAs, later when they wait for the turn
+      constexpr int kAddEarly = NB1 + SA::NDK / 4;
+      constexpr int kAddLate = NB1 + (3 * SA::NDK) / 4;
       f32x16 dqAcc[C::MQD];
 #pragma unroll
       for (int m = 0; m < C::MQD; ++m) dqAcc[m] = f32x16{};
-      {
-        bf16x8 ad[C::MQD];
-#pragma unroll
-        for (int m = 0; m < C::MQD; ++m) ad[m] = frag_tr_s<C::NCH_S>(sdS, 0, 32 * (mq0 + m), false);
-#pragma unroll
-        for (int s = 0; s < C::KKV; ++s) {
-          bf16x8 adn[C::MQD];
-#pragma unroll
-          for (int m = 0; m < C::MQD; ++m)
-            adn[m] = s + 1 < C::KKV ? frag_tr_s<C::NCH_S>(sdS, 16 * (s + 1), 32 * (mq0 + m), false) : ad[m];
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int m = 0; m < C::MQD; ++m) dqAcc[m] = mfma32(ad[m], kTB[s], dqAcc[m]);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int m = 0; m < C::MQD; ++m) ad[m] = adn[m];
-        }
-      }
-      trace_rec(2, t, gidx);
+      float old[C::MQD][16];
+      // accumulator of dQ tile i: uniform base + 32-bit per-lane byte offset
+      unsigned char* dqbase = reinterpret_cast<unsigned char*>(a.dqacc + head_off + qrow0 * D);
 
-      // ---- add the partial into dQ tile i's fp32 accumulator ----
-      float* dqt = a.dqacc + head_off + qrow0 * D + 32 * nbq + c32;
-      if constexpr (DQM == kDqUnordered) {
-        __builtin_amdgcn_sched_barrier(0);  // same scheduling region boundary as the ordered modes' turn wait
-#pragma unroll
-        for (int m = 0; m < C::MQD; ++m)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qloc = 32 * (mq0 + m) + 8 * (r >> 2) + 4 * g + (r & 3);
-            __hip_atomic_fetch_add(dqt + (long long)qloc * D, dqAcc[m][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-      } else {
+      auto loadB = [&](auto kc, Opnd& o) {
+        constexpr int k = decltype(kc)::value;
+        if constexpr (k < NB1) {
+          constexpr int m = k % C::MQD, s = k / C::MQD;
+          o.lo = lds_tr_asm<16 * s * C::PS + 64 * m>(aS);
+          o.hi = lds_tr_asm<(16 * s + 4) * C::PS + 64 * m>(aS);
+        } else {
+          constexpr int x = k - NB1, kind = 2 + (x & 1), st = x >> 1;
+          constexpr int sq = 2 * (C::MQ - 1) + st / C::ND, n = st % C::ND;
+          constexpr int off = (kind == 2 ? C::QB : 0) + 16 * sq * C::PD + 64 * n;
+          o.lo = lds_tr_asm<off>(aT);
+          o.hi = lds_tr_asm<off + 8 * C::PD>(aT);
+        }
+      };
+      auto mfmaB = [&](auto kc, const u32x4& opr) {
+        constexpr int k = decltype(kc)::value;
+        const bf16x8 op = as_bf16x8(opr);
+        if constexpr (k < NB1) {
+          constexpr int m = k % C::MQD, s = k / C::MQD;
+          dqAcc[m] = mfma32(op, kTB[s], dqAcc[m]);
+        } else {
+          constexpr int x = k - NB1, kind = 2 + (x & 1), st = x >> 1;
+          constexpr int sq = 2 * (C::MQ - 1) + st / C::ND, n = st % C::ND;
+          if constexpr (kind == 2) mfma_agpr(dVacc[n], pB[sq], opr);
+          else mfma_agpr(dKacc[n], dsB[sq], opr);
+        }
+      };
+      // (uniform row base) + (32-bit lane offset): global accesses with an SGPR base
+      auto dqp = [&](int m, int r) -> float* {
+        unsigned char* row = dqbase + (32 * m + 8 * (r >> 2) + (r & 3)) * D * 4;
+        return reinterpret_cast<float*>(row + (size_t)(uint32_t)dqlane);
+      };
+
+      // wait for the turn of this workgroup's partial in dQ tile i's order
+      auto turn = [&]() {
         if (lane == 0) {
           if (a.delay_seed) {
             const long long until = now_ticks() + (hash3(a.delay_seed, (unsigned)gidx, (unsigned)(t * 4 + w)) & 1023u);
@@ -435,64 +739,136 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
           }
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        trace_rec(3, t, gidx);
-        if (rk == 0) {
-#pragma unroll
-          for (int m = 0; m < C::MQD; ++m)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int qloc = 32 * (mq0 + m) + 8 * (r >> 2) + 4 * g + (r & 3);
-              __hip_atomic_store(dqt + (long long)qloc * D, dqAcc[m][r], __ATOMIC_RELAXED, kScope);
-            }
-        } else if constexpr (DQM == kDqOrderedAtomic) {
-#pragma unroll
-          for (int m = 0; m < C::MQD; ++m)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int qloc = 32 * (mq0 + m) + 8 * (r >> 2) + 4 * g + (r & 3);
-              __hip_atomic_fetch_add(dqt + (long long)qloc * D, dqAcc[m][r], __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-            }
-        } else {
+      };
+      // RMW modes: read the accumulator (after the turn has come)
+      auto rmw_loads = [&]() {
+        if (rk > 0) {
           if constexpr (DQM == kDqLocalRmw) asm volatile("buffer_inv sc0" ::: "memory");
-          float old[C::MQD][16];
 #pragma unroll
           for (int m = 0; m < C::MQD; ++m)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int qloc = 32 * (mq0 + m) + 8 * (r >> 2) + 4 * g + (r & 3);
-              old[m][r] = __hip_atomic_load(dqt + (long long)qloc * D, __ATOMIC_RELAXED, kScope);
-            }
+            for (int r = 0; r < 16; ++r) old[m][r] = __hip_atomic_load(dqp(m, r), __ATOMIC_RELAXED, kScope);
+        } else {
 #pragma unroll
           for (int m = 0; m < C::MQD; ++m)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int qloc = 32 * (mq0 + m) + 8 * (r >> 2) + 4 * g + (r & 3);
-              __hip_atomic_store(dqt + (long long)qloc * D, old[m][r] + dqAcc[m][r], __ATOMIC_RELAXED, kScope);
-            }
+            for (int r = 0; r < 16; ++r) old[m][r] = 0.f;
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        const bool withhold = (a.skip_item >= 0 && gidx == a.skip_item && t == 0);
-        pend_flag = withhold ? nullptr : flag;
-        pend_val = rk + 1;
+      };
+      // after the dQ MFMAs: wait for the turn if it had not come (RMW: then read
+      // the accumulator), or issue the adds themselves (atomic modes)
+      auto adds_begin = [&]() {
+        if constexpr (DQM == kDqUnordered) {
+#pragma unroll
+          for (int m = 0; m < C::MQD; ++m)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              __hip_atomic_fetch_add(dqp(m, r), dqAcc[m][r], __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          if (!early) {
+            turn();
+            trace_rec(3, t, gidx);
+            if constexpr (kRmw) rmw_loads();
+          }
+          if constexpr (!kRmw) {  // ordered atomic adds; the first contributor stores
+            if (rk == 0) {
+#pragma unroll
+              for (int m = 0; m < C::MQD; ++m)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                  __hip_atomic_store(dqp(m, r), dqAcc[m][r], __ATOMIC_RELAXED, kScope);
+            } else {
+#pragma unroll
+              for (int m = 0; m < C::MQD; ++m)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                  __hip_atomic_fetch_add(dqp(m, r), dqAcc[m][r], __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+            }
+          }
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        }
+      };
+      auto adds_finish = [&]() {
+        if constexpr (kRmw) {
+#pragma unroll
+          for (int m = 0; m < C::MQD; ++m)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              __hip_atomic_store(dqp(m, r), old[m][r] + dqAcc[m][r], __ATOMIC_RELAXED,
+                                 kScope);
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        }
+        if constexpr (DQM != kDqUnordered) {
+          const bool withhold = (a.skip_item >= 0 && gidx == a.skip_item && t == 0);
+          pend_flag = withhold ? nullptr : flag;
+          pend_val = rk + 1;
+        }
+        trace_rec(4, t, gidx);
+        // Prefetch tile t+2 into the buffer tile t-1 used. Issued after the
+        // adds, so waiting for the adds (next tile top) or for later loads
+        // never waits for this DMA.
+        dma_pending = t + 2 < t_end;
+        if (dma_pending) {
+          int ni, nj;
+          sc.tile(it, t + 2, ni, nj);
+          dma_q(b == 0 ? 2 : b - 1, head_off, bhS, ni);
+        }
+      };
+
+      if constexpr (kRmw) {
+        if (early) {
+          trace_rec(3, t, gidx);
+          rmw_loads();
+        }
       }
-      trace_rec(4, t, gidx);
-      // the last block's dV/dK runs while the adds are in flight
-      dvdk(C::MQ - 1);
+      static_for<0, PF>([&](auto kc) { loadB(kc, ring[decltype(kc)::value]); });
+      static_for<0, NB>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        if constexpr (k == NB1) {
+          DETATTN_FENCE();
+          trace_rec(2, t, gidx);
+          adds_begin();
+          DETATTN_FENCE();
+        }
+        if constexpr (kRmw && k == kAddEarly) {
+          if (early) adds_finish();
+          DETATTN_FENCE();
+        }
+        if constexpr (k == kAddLate) {
+          if (!kRmw || !early) adds_finish();
+          DETATTN_FENCE();
+        }
+        if constexpr (k + PF < NB) loadB(std::integral_constant<int, k + PF>{}, ring[(k + PF) % RING]);
+        Opnd& o = ring[k % RING];
+        lgkm_wait<2 * (k + PF < NB ? PF : NB - 1 - k)>(o.lo, o.hi);  // two reads per operand
+        mfmaB(kc, cat2(o.lo, o.hi));
+        DETATTN_FENCE();
+      });
 
       trace_rec(5, t, gidx);
       ++t;
       if (t >= t_end) break;
-      // the next tile's DMA (issued during this tile) and this tile's
-      // accumulator adds are complete in every wave
-      wait_vm_all();
-      __syncthreads();
-      if (tid == 0 && pend_flag)
-        __hip_atomic_store(pend_flag, pend_val, __ATOMIC_RELAXED, kFlagScope);
+      b = b == 2 ? 0 : b + 1;
+      // The next tile's DMA (issued during the previous tile) and this tile's
+      // accumulator adds are complete in every wave; the DMA issued during
+      // this tile (the newest vector-memory operations) may stay in flight.
+      if (dma_pending) {
+        if (w == 0) vm_barrier<C::dma_ops(0)>();
+        else if (w == 1) vm_barrier<C::dma_ops(1)>();
+        else if (w == 2) vm_barrier<C::dma_ops(2)>();
+        else vm_barrier<C::dma_ops(3)>();
+      } else {
+        vm_barrier<0>();
+      }
+      if (tid == 0 && pend_flag) __hip_atomic_store(pend_flag, pend_val, __ATOMIC_RELAXED, kFlagScope);
       pend_flag = nullptr;
     } while (true);  // tiles of the segment
 
     // ---- end of a column: publish, then dK, dV of KV tile j to global ----
+    mfma_agpr_drain();
     wait_vm_all();
     __syncthreads();
     if (tid == 0 && pend_flag) __hip_atomic_store(pend_flag, pend_val, __ATOMIC_RELAXED, kFlagScope);
@@ -507,5 +883,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     }  // segments
   }  // items
 }
+
+#undef DETATTN_FENCE
 
 }  // namespace detattn

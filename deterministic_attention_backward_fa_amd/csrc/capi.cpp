@@ -221,16 +221,16 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   unsigned* header = reinterpret_cast<unsigned*>(ws);
   int* flags = reinterpret_cast<int*>(ws + L.flags_off);
-  float* delta = reinterpret_cast<float*>(ws + L.delta_off);
-  float* lse2 = reinterpret_cast<float*>(ws + L.lse2_off);
+  float* ndelta = reinterpret_cast<float*>(ws + L.ndelta_off);
+  float* nlse = reinterpret_cast<float*>(ws + L.nlse_off);
   float* dqacc = reinterpret_cast<float*>(ws + L.dqacc_off);
   hipStream_t st_ = static_cast<hipStream_t>(stream);
   const long long rows = BH * s.S;
   const long long elems = rows * s.D;
   const bool unordered = P.dqm_internal == kDqUnordered;
 
-  hipError_t e = launch_pre(s.D, static_cast<const __bf16*>(o), static_cast<const __bf16*>(dout), lse, lse2, delta,
-                            rows, flags,
+  hipError_t e = launch_pre(s.D, static_cast<const __bf16*>(o), static_cast<const __bf16*>(dout), lse, 1.f / s.softmax_scale,
+                            nlse, ndelta, rows, flags,
                             BH * P.pub.n_q, header, unordered ? dqacc : nullptr, elems, st_);
   if (e != hipSuccess) return DETATTN_ERR_HIP;
 
@@ -241,8 +241,8 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
   a.k = static_cast<const __bf16*>(k);
   a.v = static_cast<const __bf16*>(v);
   a.dout = static_cast<const __bf16*>(dout);
-  a.lse2 = lse2;
-  a.delta = delta;
+  a.nlse = nlse;
+  a.ndelta = ndelta;
   a.dqacc = dqacc;
   a.dk = static_cast<__bf16*>(dk);
   a.dv = static_cast<__bf16*>(dv);

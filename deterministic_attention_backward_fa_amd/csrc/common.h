@@ -202,15 +202,15 @@ struct WsLayout {
   static constexpr size_t kHeader = 256;         // ticket @0, error word @64, error detail @128
   static constexpr size_t kFlagStride = 128;     // one L2 line per dQ tile flag
   static constexpr size_t kMinBlockQ = 64;
-  size_t flags_off, flags_bytes, delta_off, delta_bytes, lse2_off, dqacc_off, dqacc_bytes, total;
+  size_t flags_off, flags_bytes, ndelta_off, row_bytes, nlse_off, dqacc_off, dqacc_bytes, total;
   __host__ __device__ WsLayout(long long BH, long long S, long long D) {
     flags_off = kHeader;
     long long nq_max = (S + (long long)kMinBlockQ - 1) / (long long)kMinBlockQ;
     flags_bytes = (size_t)(BH * nq_max) * kFlagStride;
-    delta_off = align(flags_off + flags_bytes);
-    delta_bytes = (size_t)(BH * S) * 4;
-    lse2_off = align(delta_off + delta_bytes);  // LSE * log2(e), same size as delta
-    dqacc_off = align(lse2_off + delta_bytes);
+    ndelta_off = align(flags_off + flags_bytes);  // -D per row
+    row_bytes = (size_t)(BH * S) * 4;
+    nlse_off = align(ndelta_off + row_bytes);     // -LSE / scale per row
+    dqacc_off = align(nlse_off + row_bytes);
     dqacc_bytes = (size_t)(BH * S * D) * 4;
     total = align(dqacc_off + dqacc_bytes);
   }

@@ -26,7 +26,8 @@ struct MainInfo {
 MainInfo main_info_d64(int BQ, int BKV, int causal, int dq_mode);
 MainInfo main_info_d128(int BQ, int BKV, int causal, int dq_mode);
 
-hipError_t launch_pre(int D, const __bf16* o, const __bf16* dout, const float* lse, float* lse2, float* delta,
+hipError_t launch_pre(int D, const __bf16* o, const __bf16* dout, const float* lse, float inv_scale, float* nlse,
+                      float* ndelta,
                       long long rows, int* flags,
                       long long n_flags, unsigned* header, float* dqacc, long long dqacc_elems, hipStream_t st);
 hipError_t launch_convert(const float* acc, __bf16* dq, long long elems, float scale, hipStream_t st);

@@ -12,12 +12,18 @@ import torch
 
 PHASES = {0: "tile_top", 1: "ds_ready", 2: "dq_done", 3: "turn", 4: "adds_issued", 5: "tile_end", 6: "seg_begin",
           7: "seg_end"}
-# consecutive phase pairs inside one tile, and the name of the interval
+# consecutive phase pairs inside one tile, and the name of the interval. A
+# tile whose turn had already come at its top reads the accumulator right
+# after the dS^T barrier (phase 3 before phase 2); the others wait after the
+# dQ MFMAs.
 INTERVALS = [
     (0, 1, "S,dP MFMA + P,dS VALU + dS^T store"),
     (1, 2, "barrier + dQ MFMA issue"),
     (2, 3, "wait for the dQ tile's turn"),
     (3, 4, "accumulator adds issued"),
+    (1, 3, "barrier (turn already come)"),
+    (3, 2, "accumulator reads + dQ MFMA issue"),
+    (2, 4, "dV,dK MFMA issue up to the adds"),
     (4, 5, "dV,dK MFMA issue"),
     (5, 0, "drain + barrier + publish (to next tile)"),
 ]
