@@ -256,7 +256,9 @@ def main():
 
         recs, _ = dtrace.collect(da, tensors, causal, headline)
         summ = dtrace.summarize(recs)
-        log(f"[bench] trace {headline}: {summ['mean_ticks_per_tile']:.0f} ticks/tile over {summ['workgroups']} WGs")
+        log(f"[bench] trace {headline}: tile period median {summ['tile_period_median']:.0f} ticks, "
+            f"{summ['early_turn_fraction'] * 100:.0f}% of tiles find their turn at the dS^T barrier "
+            f"({summ['workgroups']} WGs)")
         for name, share in summ["share"].items():
             log(f"[bench]   {share * 100:5.1f}%  {summ['ticks'][name]:8.0f}  {name}")
         line["trace_share"] = {k: round(v, 4) for k, v in summ["share"].items()}

@@ -11,6 +11,7 @@ MainInfo info_of() {
     auto fn = &bwd_main_kernel<D, BQ, BKV, CAUSAL, DQM>;
     m.func = reinterpret_cast<const void*>(fn);
     m.lds_bytes = MainCfg<D, BQ, BKV>::LDS_BYTES;
+    m.tcopy = MainCfg<D, BQ, BKV>::TCOPY ? 1 : 0;
     int occ = 0;
     if (hipFuncSetAttribute(m.func, hipFuncAttributeMaxDynamicSharedMemorySize, m.lds_bytes) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kThreads, m.lds_bytes) != hipSuccess)
@@ -35,7 +36,7 @@ MainInfo pick(int causal, int dqm) {
     if (dqm == kDqUnordered) return info_of<64, BQ, BKV, false, kDqUnordered>();
     if (dqm == kDqLocalRmw) return info_of<64, BQ, BKV, false, kDqLocalRmw>();
   }
-  return MainInfo{nullptr, 0, 0};
+  return MainInfo{nullptr, 0, 0, 0};
 }
 
 }  // namespace
@@ -45,7 +46,7 @@ MainInfo main_info_d64(int BQ, int BKV, int causal, int dq_mode) {
   if (BQ == bq && BKV == bkv) return pick<bq, bkv>(causal, dq_mode);
   X(64, 64) X(128, 128) X(64, 128)
 #undef X
-  return MainInfo{nullptr, 0, 0};
+  return MainInfo{nullptr, 0, 0, 0};
 }
 
 }  // namespace detattn

@@ -50,6 +50,25 @@
 
 #include <type_traits>
 
+// Scheduling parameters of the instruction streams (measured choices; the
+// macros exist so variants can be compiled side by side):
+//   PF         LDS operand loads run this many operands ahead of their MFMA
+//   ELEM_DELAY MFMAs of a group issued before its first elementwise unit
+//   DMA_SPAN   the next tile's DMA is spread over this fraction (1/8ths) of stream A
+//   ADD_EARLY  dV/dK MFMAs (1/8ths of them) issued before the early accumulator adds
+#ifndef DETATTN_PF
+#define DETATTN_PF 4
+#endif
+#ifndef DETATTN_ELEM_DELAY
+#define DETATTN_ELEM_DELAY 1
+#endif
+#ifndef DETATTN_DMA_SPAN
+#define DETATTN_DMA_SPAN 4
+#endif
+#ifndef DETATTN_ADD_EARLY
+#define DETATTN_ADD_EARLY 2
+#endif
+
 namespace detattn {
 
 template <int D, int BQ, int BKV>
@@ -62,33 +81,52 @@ struct MainCfg {
   static constexpr int ND = D / 32;      // 32-column blocks over D
   static constexpr int KQ = QW / 16;     // MFMA K steps over the wave's Q rows
   static constexpr int KKV = BKV / 16;   // MFMA K steps over the KV tile
-  static constexpr int WPD = 4 / ND;     // waves per D block of the dQ tile
-  static constexpr int MQD = (BQ / 32) / WPD;
+  // dQ partial (BQ x D) split over the 4 waves: each wave owns DW 32-column
+  // blocks x MQD 32-row blocks. Two column blocks per wave (when the tile has
+  // enough blocks) let one dS operand read feed two MFMAs.
+  static constexpr int DW = (ND >= 2 && ND * (BQ / 32) >= 8) ? 2 : 1;
+  static constexpr int MQD = ND * (BQ / 32) / (4 * DW);
+  static constexpr int DGRP = ND / DW;   // column-block groups
   static constexpr int NCH = D / 8;      // 16-byte chunks per Q/dO/K/V row
   static constexpr int PD = D * 2 + 16;  // padded row pitch of Q/dO/K/V tiles (bytes)
-  static constexpr int PS = BQ * 2 + 16; // padded row pitch of the dS^T tile (bytes)
+  static constexpr int NCH_S = BQ / 8;   // 16-byte chunks per dS^T row
+  static constexpr int PS = BQ * 2;      // dS^T row pitch (bytes; XOR-swizzled chunks, see swz_f)
   static constexpr int QB = BQ * PD;     // one Q or dO tile
   static constexpr int KB = BKV * PD;    // one K or V tile
   static constexpr int SB = BKV * PS;    // dS^T tile (row kv, column q)
   static constexpr int LDB = BQ * 8;     // -LSE/scale then -D, fp32
-  static constexpr int BUF = 2 * QB + LDB;  // one Q-tile buffer: Q, dO, row terms
+  // Transposed copies of Q and dO ([D][BQ] per tile, padded rows) feed the dV,
+  // dK products with 16-byte reads; without them those operands are read
+  // from the row tiles with transposing reads (used where LDS is too small).
+  static constexpr int PT = BQ * 2 + 16;
+  static constexpr int QTB = D * PT;
+  // Measured on MI355X: the extra DMA traffic of the copies costs more than
+  // the transposing reads they replace, so they are off.
+  static constexpr bool kUseTransposedCopies = false;
+  static constexpr bool TCOPY = kUseTransposedCopies && SB + 2 * (2 * QB + 2 * QTB + LDB) + 16 <= 160 * 1024;
+  static constexpr int OFF_QT = 2 * QB;  // inside a buffer (TCOPY)
+  static constexpr int OFF_LD = 2 * QB + (TCOPY ? 2 * QTB : 0);
+  static constexpr int BUF = OFF_LD + LDB;  // one Q-tile buffer: Q, dO, [Q^T, dO^T], row terms
   static constexpr int OFF_DS = 0;
-  static constexpr int OFF_B0 = SB;      // buffer b (0..2) at OFF_B0 + b * BUF
-  // K_j, V_j are staged in buffers 1-2 at the start of a column (they move to
+  // Q-tile buffers: the next tile is loaded one tile ahead; a third buffer
+  // (when LDS allows) gives K_j, V_j room to be staged at the start of a
+  // column next to the first Q tile
+  static constexpr int NBUF = TCOPY ? 2 : 3;
+  static constexpr int OFF_B0 = SB;      // buffer b at OFF_B0 + b * BUF
+  // K_j, V_j are staged in buffers 1.. at the start of a column (they move to
   // registers before those buffers receive Q tiles)
   static constexpr int OFF_K = OFF_B0 + BUF;
   static constexpr int OFF_V = OFF_K + KB;
-  static constexpr int TILE_END = OFF_B0 + 3 * BUF;
+  static constexpr int TILE_END = OFF_B0 + NBUF * BUF;
   static constexpr int DMA_Q = BQ * (NCH + 1) / 64;  // 1 KB DMA instructions per padded Q/dO tile
   static constexpr int DMA_K = BKV * (NCH + 1) / 64;
   static constexpr int DMA_QW = (DMA_Q + 3) / 4;     // per wave, at most
-  // vector-memory instructions one wave issues for one Q tile (Q and dO rows,
-  // plus the row terms on waves 0 and 1)
-  static constexpr int dma_ops(int w) {
-    int n = 0;
-    for (int x = w; x < DMA_Q; x += 4) n += 2;
-    return n + (w < 2 ? BQ / 64 : 0);
-  }
+  static constexpr int NCT = BQ / 8;                 // 16-byte chunks per transposed row
+  static constexpr int DMA_T = D * (NCT + 1) / 64;   // per padded transposed tile
+  static constexpr int DMA_TW = (DMA_T + 3) / 4;
+  // DMA work of one wave for one Q tile, in slots issued one by one between
+  // MFMAs: Q and dO rows, the transposed copies (TCOPY), the row terms
+  static constexpr int DMA_SLOTS = 2 * DMA_QW + (TCOPY ? 2 * DMA_TW : 0) + 1;
   // Epilogue scratch, aliasing the tile buffers (nothing is in flight then):
   // per output tensor, the fp32 partials of the waves with wq == 1 (NQW == 2)
   // and a padded bf16 tile for coalesced stores.
@@ -99,11 +137,12 @@ struct MainCfg {
   static constexpr int OFF_MISC = TILE_END > EPI_END ? TILE_END : EPI_END;
   static constexpr int LDS_BYTES = OFF_MISC + 16;
   static_assert(NKVW * NQW == 4, "4 waves");
-  static_assert(QW % 32 == 0 && MQD >= 1, "tile shape");
+  static_assert(QW % 32 == 0 && MQD >= 1 && DGRP * DW == ND && 4 * DW * MQD == ND * (BQ / 32), "tile shape");
+  static_assert(MQD == 1, "one dS row block per wave (the swizzled dS reads use per-lane offsets)");
   static_assert((BQ * (NCH + 1)) % 64 == 0 && (BKV * (NCH + 1)) % 64 == 0, "DMA granularity");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(OFF_V + KB <= TILE_END, "K, V staging");
-  static_assert(dma_ops(0) <= 63, "vmcnt field");
+  static_assert(!TCOPY || (D * (NCT + 1)) % 64 == 0, "DMA granularity");
 };
 
 // Order of the MFMAs of stream A (before the dS^T barrier). Group gi holds the
@@ -135,7 +174,7 @@ struct StreamA {
   static constexpr int step(int k) { return sdp(k) ? (rel(k) >> 1) : (drel(k) >> 1); }
   // LDS instructions of MFMA k's operand load, and those issued after it by
   // the time MFMA k runs (operands are loaded pf MFMAs ahead)
-  static constexpr int nloads(int k) { return sdp(k) ? 1 : 2; }
+  static constexpr int nloads(int k) { return (sdp(k) || C::TCOPY) ? 1 : 2; }
   static constexpr int loads_after(int k, int pf) {
     int n = 0;
     for (int x = k + 1; x <= k + pf && x < N; ++x) n += nloads(x);
@@ -144,14 +183,50 @@ struct StreamA {
   // elementwise units (16 elements + 4 dS^T stores) issued after the j-th MFMA
   // of a group of size G: the first DELAY MFMAs of the group carry none, so
   // the previous group's last results have landed.
+  // DMA slots of the next Q tile issued after MFMA k: spread evenly over the
+  // stream from MFMA 1 on, so the texture path is never flooded
+  static constexpr int dma_before(int k) {
+    const int U = C::DMA_SLOTS, S0 = 1;
+    const int E = S0 + 1 + ((N - S0 - 1) * DETATTN_DMA_SPAN) / 8;  // all slots issued by MFMA E
+    if (k <= S0) return 0;
+    if (k >= E) return U;
+    const int v = ((k - S0) * U + (E - S0 - 1)) / (E - S0);
+    return v < U ? v : U;
+  }
   static constexpr int kUnits = 20;
-  static constexpr int kDelay = 1;
+  static constexpr int kDelay = DETATTN_ELEM_DELAY;
   static constexpr int units_before(int j, int G) {
     return j <= kDelay ? 0 : (j >= G ? kUnits : ((j - kDelay) * kUnits) / (G - kDelay));
   }
 };
 
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
+
+// Order of the MFMAs of stream B (after the dS^T barrier): the dQ partial
+// (KKV K steps x MQD row blocks x DW column blocks; one dS operand, read with
+// two transposing reads, serves the DW column blocks), then the dV/dK MFMAs
+// of the last row block (one operand each). Loads are numbered separately
+// from MFMAs: MFMA k uses load load_of(k), and loads run pf loads ahead.
+template <class C>
+struct StreamB {
+  static constexpr int NB1 = C::KKV * C::MQD * C::DW;  // dQ MFMAs
+  static constexpr int N = NB1 + 4 * C::ND;
+  static constexpr int NL1 = C::KKV * C::MQD;          // dQ operand loads
+  static constexpr int NL = NL1 + 4 * C::ND;
+  static constexpr int load_of(int k) { return k < NB1 ? k / C::DW : NL1 + (k - NB1); }
+  static constexpr bool first_use(int k) { return k >= NB1 || k % C::DW == 0; }
+  static constexpr int ninst(int l) { return (l >= NL1 && C::TCOPY) ? 1 : 2; }  // LDS instructions of load l
+  // last load issued before MFMA k runs
+  static constexpr int issued_by(int k, int pf) {
+    const int x = load_of(k) + pf;
+    return x < NL - 1 ? x : NL - 1;
+  }
+  static constexpr int insts_after(int k, int pf) {
+    int n = 0;
+    for (int l = load_of(k) + 1; l <= issued_by(k, pf); ++l) n += ninst(l);
+    return n;
+  }
+};
 
 template <int B, int E, class F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -308,15 +383,29 @@ __device__ __forceinline__ void store_column(f32x16 (&acc)[C::ND], float mul, __
   __syncthreads();
 }
 
+// Q, dO, K, V tiles in LDS: rows padded by 16 bytes, and inside every 16-row
+// block logical row r sits at physical row rperm(r) = 4*(r%4) + (r/4)%4 (an
+// involution). With the 272-byte (D = 128) or 144-byte (D = 64) pitch each row
+// starts 4 (or 36) banks after the previous one, so
+//  * 16 consecutive logical rows read at one 16-byte column (row fragments)
+//    cover all 64 banks once, and
+//  * the four logical rows a 16-lane group reads transposed (4j + g .. for
+//    rows 4g..4g+3) start 16 banks apart, each group's 32-byte reads of two
+//    16-lane groups filling the 64 banks once;
+// logical row r + 8 sits 2 physical rows after r, r + 4 one row after (for r
+// with (r/4)%4 even), and multiples of 16 are unchanged, so those steps stay
+// compile-time offsets.
+__host__ __device__ constexpr int rperm(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
+
 // Global byte offset, inside a row-major tile of NCH-chunk rows, of the chunk
-// that lane `lane` of DMA instruction `ins` moves into the padded LDS tile
-// (NCH + 1 chunks per row). Padding chunks re-read chunk 0 of their row; those
-// bytes land in the padding and are never read.
+// that lane `lane` of DMA instruction `ins` moves into the padded, row-permuted
+// LDS tile (NCH + 1 chunks per row). Padding chunks re-read chunk 0 of their
+// row; those bytes land in the padding and are never read.
 template <int NCH>
 __device__ __forceinline__ int dma_goff(int ins, int lane) {
   const int p = ins * 64 + lane;
   const int row = p / (NCH + 1), col = p % (NCH + 1);
-  return row * (NCH * 16) + (col < NCH ? col : 0) * 16;
+  return rperm(row) * (NCH * 16) + (col < NCH ? col : 0) * 16;
 }
 
 __device__ __forceinline__ void dma16(const void* gsrc, void* lds) {
@@ -327,7 +416,7 @@ template <int D, int BQ, int BKV, bool CAUSAL, int DQM>
 __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   using C = MainCfg<D, BQ, BKV>;
   using SA = StreamA<C>;
-  constexpr int PF = 4;       // LDS operand loads run this many MFMAs ahead
+  constexpr int PF = DETATTN_PF;  // LDS operand loads run this many MFMAs ahead
   constexpr int RING = PF + 2;  // operand registers; a slot is reloaded two MFMAs after its last reader
   // Scope of the accumulator accesses: across XCDs (sc1), or inside the XCD's
   // L2 (sc0) when every workgroup of a ring runs on one XCD. sc0 loads may hit
@@ -336,6 +425,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   constexpr int kScope = DQM == kDqLocalRmw ? __HIP_MEMORY_SCOPE_WORKGROUP : __HIP_MEMORY_SCOPE_AGENT;
   constexpr int kFlagScope = __HIP_MEMORY_SCOPE_AGENT;
   constexpr bool kRmw = DQM == kDqOrderedRmw || DQM == kDqLocalRmw;
+  constexpr int kWaves = kThreads / 64;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   int* sMisc = reinterpret_cast<int*>(smem + C::OFF_MISC);
 
@@ -348,8 +438,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   const int grp = lane >> 4;
   const int wk = w % C::NKVW;
   const int wq = w / C::NKVW;
-  const int nbq = w % C::ND;             // dQ: this wave's D block
-  const int mq0 = (w / C::ND) * C::MQD;  // dQ: first 32-row block
+  const int nbq = (w % C::DGRP) * C::DW;    // dQ: this wave's first D block
+  const int mq0 = (w / C::DGRP) * C::MQD;  // dQ: first 32-row block
   const float c1 = a.scale * kLog2e;
   const Sched sc = a.sc;
   const int ipH = sc.items_per_head();
@@ -358,15 +448,43 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   // Per-lane LDS byte offsets; everything else in a fragment address is a
   // compile-time offset (or the per-tile buffer base).
   const int trcol = (16 * (grp & 1) + 4 * (s16 & 3)) * 2;
-  const int oA = (C::QW * wq + c32) * C::PD + g * 16;                // Q/dO row fragments (buffer-relative)
-  const int oT = (C::QW * wq + 4 * g + (s16 >> 2)) * C::PD + trcol;  // Q/dO transposed fragments, accumulator K order
-  const int oS = C::OFF_DS + (8 * g + (s16 >> 2)) * C::PS + trcol + 64 * mq0;     // dS transposed fragments
-  const int oW = C::OFF_DS + (32 * wk + c32) * C::PS + (C::QW * wq + 4 * g) * 2;  // dS^T stores
-  const int oL = 2 * C::QB + (C::QW * wq + 4 * g) * 4;                            // row terms (buffer-relative)
+  // Q/dO row fragments (buffer-relative): logical row QW*wq + lane%32
+  const int oA = rperm(C::QW * wq + c32) * C::PD + g * 16;
+  // Q/dO transposed fragments in accumulator K order: logical rows 4g + j
+  // (j = lane%16 / 4) at physical 4j + g; rows + 8 at physical + 2
+  const int oT = (C::QW * wq + 4 * (s16 >> 2) + g) * C::PD + trcol;
+  // dS^T (row kv, column q; chunk c of row r at c ^ swz_f(r)): transposed
+  // fragments of the dQ product read rows 8g + j (lo) and 8g + j + 4 (hi)
+  const int sq_chunk = 4 * mq0 + 2 * (grp & 1) + ((s16 & 3) >> 1);
+  const int sr_lo = 8 * g + (s16 >> 2), sr_hi = sr_lo + 4;
+  const int oS = C::OFF_DS + sr_lo * C::PS + ((sq_chunk ^ swz_f<C::NCH_S>(sr_lo)) << 4) + (s16 & 1) * 8;
+  const int oS_hi = C::OFF_DS + sr_hi * C::PS + ((sq_chunk ^ swz_f<C::NCH_S>(sr_hi)) << 4) + (s16 & 1) * 8;
+  // dS^T stores: row 32*wk + lane%32, chunk (QW*wq + 16 sq + 8 hh) / 8, bytes 8g
+  const int w_row = 32 * wk + c32;
+  const int w_swz = swz_f<C::NCH_S>(w_row);
+  const int oW = C::OFF_DS + w_row * C::PS + 8 * g;
+  const int oL = C::OFF_LD + (C::QW * wq + 4 * g) * 4;                           // row terms (buffer-relative)
+  const int oQT = C::OFF_QT + c32 * C::PT + g * 16 + C::QW * wq * 2;              // Q^T, dO^T fragments (TCOPY)
   const int dqlane = ((32 * mq0 + 4 * g) * D + 32 * nbq + c32) * 4;  // dQ accumulator tile, per lane
   int goffQ[C::DMA_QW];
 #pragma unroll
   for (int x = 0; x < C::DMA_QW; ++x) goffQ[x] = dma_goff<C::NCH>(w + 4 * x, lane);
+  // transposed tiles: D rows of BQ elements, S elements apart in global memory
+  int goffT[C::TCOPY ? C::DMA_TW : 1];
+  if constexpr (C::TCOPY) {
+#pragma unroll
+    for (int x = 0; x < C::DMA_TW; ++x) {
+      const int p = (w + 4 * x) * 64 + lane;
+      const int row = p / (C::NCT + 1), col = p % (C::NCT + 1);
+      goffT[x] = row * a.S * 2 + (col < C::NCT ? col : 0) * 16;
+    }
+  }
+  int goffT_last = 0;  // the last transposed-tile instruction (repeated by waves with fewer)
+  if constexpr (C::TCOPY) {
+    const int p = (C::DMA_T - 1) * 64 + lane;
+    const int row = p / (C::NCT + 1), col = p % (C::NCT + 1);
+    goffT_last = row * a.S * 2 + (col < C::NCT ? col : 0) * 16;
+  }
 
   int ring_id = 0, slot = 0;
   if (!a.ticket_mode) {
@@ -391,7 +509,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
 
   auto ld16 = [&](int off) -> bf16x8 { return *reinterpret_cast<const bf16x8*>(smem + off); };
   const uint32_t lbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)smem;
-  const uint32_t aS = lbase + oS;
+  const uint32_t aS = lbase + oS, aS_hi = lbase + oS_hi;
   auto ldtr = [&](int off) -> bf16x4 { return lds_read_tr(reinterpret_cast<const __bf16*>(smem + off)); };
 
   // Q, dO and the row terms of Q tile i -> buffer b (asynchronous).
@@ -409,7 +527,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
         dma16(gd + (uint32_t)goffQ[x], base + C::QB + ins * 1024);
       }
     }
-    float* ld = reinterpret_cast<float*>(base + 2 * C::QB);
+    if constexpr (C::TCOPY) {
+      const unsigned char* gqt = reinterpret_cast<const unsigned char*>(a.qt + head_off + qrow0);
+      const unsigned char* gdt = reinterpret_cast<const unsigned char*>(a.dot + head_off + qrow0);
+#pragma unroll
+      for (int x = 0; x < C::DMA_TW; ++x) {
+        const int ins = w + 4 * x;
+        if (ins < C::DMA_T) {
+          dma16(gqt + (uint32_t)goffT[x], base + C::OFF_QT + ins * 1024);
+          dma16(gdt + (uint32_t)goffT[x], base + C::OFF_QT + C::QTB + ins * 1024);
+        }
+      }
+    }
+    float* ld = reinterpret_cast<float*>(base + C::OFF_LD);
     dma_f32(ld, a.nlse + bhS + qrow0, BQ, 0);
     dma_f32(ld + BQ, a.ndelta + bhS + qrow0, BQ, 1);
   };
@@ -443,8 +573,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     const long long head_off = (long long)bh * a.S * D;
     const long long bhS = (long long)bh * a.S;
 
-    int* pend_flag = nullptr;  // flag of the previous tile, published once its adds are complete
-    int pend_val = 0;
 
     for (int seg = 0; seg < sc.segments(); ++seg) {
     const int t_begin = sc.seg_begin(it, seg), t_end = sc.seg_end(it, seg);
@@ -465,35 +593,37 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     __syncthreads();
     // K_j, V_j (MFMA B operands of S, dP) and K_j transposed (B operand of the
     // dQ partial) go straight into AGPRs
-    bf16x8 kB[C::KD], vB[C::KD], kTB[C::KKV];
+    bf16x8 kB[C::KD], vB[C::KD], kTB[C::KKV * C::DW];
     {
-      const uint32_t ak = lbase + C::OFF_K + (32 * wk + c32) * C::PD + g * 16;
+      const uint32_t ak = lbase + C::OFF_K + rperm(32 * wk + c32) * C::PD + g * 16;
       const uint32_t av = ak + (C::OFF_V - C::OFF_K);
-      const uint32_t akt = lbase + C::OFF_K + (8 * g + (s16 >> 2)) * C::PD + trcol + 64 * nbq;
+      // K transposed (non-permuted K order): logical rows 8g + j at physical 4j + 2g, rows + 4 at + 1
+      const uint32_t akt = lbase + C::OFF_K + (4 * (s16 >> 2) + 2 * g) * C::PD + trcol + 64 * nbq;
+      constexpr int NT = C::KKV * C::DW;  // K^T fragments: K step s, column block n at s * DW + n
       u32x4 kq[C::KD], vq[C::KD];
-      u32x2 tlo[C::KKV], thi[C::KKV];
+      u32x2 tlo[NT], thi[NT];
       static_for<0, C::KD>([&](auto sc_) {
         constexpr int s = decltype(sc_)::value;
         kq[s] = lds_ld16_agpr<32 * s>(ak);
         vq[s] = lds_ld16_agpr<32 * s>(av);
       });
-      static_for<0, C::KKV>([&](auto sc_) {
-        constexpr int s = decltype(sc_)::value;
-        tlo[s] = lds_tr_agpr<16 * s * C::PD>(akt);
-        thi[s] = lds_tr_agpr<(16 * s + 4) * C::PD>(akt);
+      static_for<0, NT>([&](auto xc) {
+        constexpr int x = decltype(xc)::value, s = x / C::DW, n = x % C::DW;
+        tlo[x] = lds_tr_agpr<16 * s * C::PD + 64 * n>(akt);
+        thi[x] = lds_tr_agpr<(16 * s + 1) * C::PD + 64 * n>(akt);
       });
       // every loaded register is tied to a wait that covers it (loads complete in order)
       static_for<0, C::KD>([&](auto sc_) {
         constexpr int s = decltype(sc_)::value;
-        constexpr int after_k = 2 * (C::KD - 1 - s) + 1 + 2 * C::KKV;
+        constexpr int after_k = 2 * (C::KD - 1 - s) + 1 + 2 * NT;
         lgkm_wait_agpr<cmin(after_k, 15)>(kq[s]);  // more loads than the counter holds: 15 is still safe
         lgkm_wait_agpr<cmin(after_k - 1, 15)>(vq[s]);
       });
-      static_for<0, C::KKV>([&](auto sc_) {
-        constexpr int s = decltype(sc_)::value;
-        constexpr int after_t = 2 * (C::KKV - 1 - s);
-        lgkm_wait_agpr<cmin(after_t + 1, 15)>(tlo[s]);
-        lgkm_wait_agpr<cmin(after_t, 15)>(thi[s]);
+      static_for<0, NT>([&](auto xc) {
+        constexpr int x = decltype(xc)::value;
+        constexpr int after_t = 2 * (NT - 1 - x);
+        lgkm_wait_agpr<cmin(after_t + 1, 15)>(tlo[x]);
+        lgkm_wait_agpr<cmin(after_t, 15)>(thi[x]);
       });
 #pragma unroll
       for (int s = 0; s < C::KD; ++s) {
@@ -503,19 +633,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
         pin_agpr(vB[s]);
       }
 #pragma unroll
-      for (int s = 0; s < C::KKV; ++s) {
-        kTB[s] = as_bf16x8(cat2(tlo[s], thi[s]));
-        pin_agpr(kTB[s]);
+      for (int x = 0; x < NT; ++x) {
+        kTB[x] = as_bf16x8(cat2(tlo[x], thi[x]));
+        pin_agpr(kTB[x]);
       }
     }
-    // K, V are in registers: buffers 1-2 are free for the next Q tiles
+    // K, V are in registers: buffer 1 is free for the next Q tile
     lds_barrier();
-    bool dma_pending = t_begin + 1 < t_end;  // this wave's newest vector-memory ops are a tile's DMA
-    if (dma_pending) {
-      int ni, nj;
-      sc.tile(it, t_begin + 1, ni, nj);
-      dma_q(1, head_off, bhS, ni);
-    }
     f32x16 dKacc[C::ND], dVacc[C::ND];
 #pragma unroll
     for (int n = 0; n < C::ND; ++n) {
@@ -531,14 +655,53 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     do {
       int i, jj;
       sc.tile(it, t, i, jj);
+      const int nb = b + 1 == C::NBUF ? 0 : b + 1;  // buffer of tile t+1
       const long long qrow0 = (long long)i * BQ;
       trace_rec(0, t, gidx);
-      // this tile's turn in dQ tile i's order: rank rk, flag = number of adds done
+      // The next tile of this column goes into the other buffer; its DMA is
+      // issued slot by slot during stream A, without branches: a wave with
+      // fewer instructions than others repeats its tile's last instruction,
+      // and in the last tile of a column the current tile is loaded again
+      // into the idle buffer (the same bytes, or bytes no one reads).
+      int ni = i;
+      if (t + 1 < t_end) {
+        int nj;
+        sc.tile(it, t + 1, ni, nj);
+      }
+      ni = __builtin_amdgcn_readfirstlane(ni);
+      const long long nrow0 = (long long)ni * BQ;
+      unsigned char* nbase = smem + C::OFF_B0 + nb * C::BUF;
+      auto dma_slot = [&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        if constexpr (u < 2 * C::DMA_QW) {
+          constexpr int x = u / 2;
+          const int ins = w + 4 * x < C::DMA_Q ? w + 4 * x : C::DMA_Q - 1;
+          const int go = w + 4 * x < C::DMA_Q ? goffQ[x] : dma_goff<C::NCH>(C::DMA_Q - 1, lane);
+          const __bf16* src = (u & 1) ? a.dout : a.q;
+          dma16(reinterpret_cast<const unsigned char*>(src + head_off + nrow0 * D) + (uint32_t)go,
+                nbase + ((u & 1) ? C::QB : 0) + ins * 1024);
+        } else if constexpr (C::TCOPY && u < 2 * C::DMA_QW + 2 * C::DMA_TW) {
+          constexpr int v = u - 2 * C::DMA_QW, x = v / 2;
+          const int ins = w + 4 * x < C::DMA_T ? w + 4 * x : C::DMA_T - 1;
+          const int go = w + 4 * x < C::DMA_T ? goffT[x] : goffT_last;
+          const __bf16* src = (v & 1) ? a.dot : a.qt;
+          dma16(reinterpret_cast<const unsigned char*>(src + head_off + nrow0) + (uint32_t)go,
+                nbase + C::OFF_QT + ((v & 1) ? C::QTB : 0) + ins * 1024);
+        } else {
+          // row terms: waves 0, 2 load -LSE/scale, waves 1, 3 load -D (duplicates write the same bytes)
+          float* ld = reinterpret_cast<float*>(nbase + C::OFF_LD) + (w & 1) * BQ;
+          const float* src = ((w & 1) ? a.ndelta : a.nlse) + bhS + nrow0;
+#pragma unroll
+          for (int x = 0; x < BQ; x += 64)
+            __builtin_amdgcn_global_load_lds((gbl_void*)(src + x + lane), (lds_void*)(ld + x), 4, 0, 0);
+        }
+      };
+      // this tile's turn in dQ tile i's order: rank rk; the flag counts the wave contributions added
       const int rk = DQM == kDqUnordered ? 0 : sc.rank(i, j);
       int* flag = a.flags + ((long long)bh * sc.n_q + i) * kFlagInts;
       const int vb = C::OFF_B0 + b * C::BUF;
       const int vL = oL + vb;
-      const uint32_t aA = lbase + oA + vb, aT = lbase + oT + vb;
+      const uint32_t aA = lbase + oA + vb, aT = lbase + oT + vb, aQT = lbase + oQT + vb;
 
       // ---- accumulator initial values: -LSE/scale (S), -D (dP); mask on diagonal tiles ----
       f32x16 sAcc[C::MQ], pAcc[C::MQ];
@@ -581,16 +744,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
         else if constexpr (kind == 1) o.q = lds_ld16_asm<C::QB + 32 * m * C::PD + 32 * st>(aA);
         else {
           constexpr int sq = 2 * m + st / C::ND, n = st % C::ND;
-          constexpr int off = (kind == 2 ? C::QB : 0) + 16 * sq * C::PD + 64 * n;
-          o.lo = lds_tr_asm<off>(aT);
-          o.hi = lds_tr_asm<off + 8 * C::PD>(aT);
+          if constexpr (C::TCOPY) {
+            // row d = 32n + lane%32 of Q^T / dO^T, Q positions 16sq + 8g .. +7
+            o.q = lds_ld16_asm<(kind == 2 ? C::QTB : 0) + 32 * n * C::PT + 32 * sq>(aQT);
+          } else {
+            constexpr int off = (kind == 2 ? C::QB : 0) + 16 * sq * C::PD + 64 * n;
+            o.lo = lds_tr_asm<off>(aT);
+            o.hi = lds_tr_asm<off + 2 * C::PD>(aT);
+          }
         }
       };
       // wait for MFMA k's operand (N = own loads issued after it) and return it
       auto waitA = [&](auto kc, Opnd& o) -> u32x4 {
         constexpr int k = decltype(kc)::value;
         constexpr int N = SA::loads_after(k, PF);
-        if constexpr (SA::sdp(k)) {
+        if constexpr (SA::sdp(k) || C::TCOPY) {
           lgkm_wait<N>(o.q);
           return o.q;
         } else {
@@ -633,7 +801,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
           bf16x4 v4;
 #pragma unroll
           for (int x = 0; x < 4; ++x) v4[x] = dsB[sq][4 * hh + x];
-          *reinterpret_cast<bf16x4*>(smem + oW + (16 * sq + 8 * hh) * 2) = v4;
+          const int chunk = (C::QW * wq) / 8 + 2 * sq + hh;
+          *reinterpret_cast<bf16x4*>(smem + oW + ((chunk ^ w_swz) << 4)) = v4;
         }
       };
 
@@ -646,6 +815,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
         if constexpr (k + PF < SA::N) loadA(std::integral_constant<int, k + PF>{}, ring[(k + PF) % RING]);
         mfmaA(kc, waitA(kc, ring[k % RING]));
         DETATTN_FENCE();
+        static_for<SA::dma_before(k), SA::dma_before(k + 1)>([&](auto uc) { dma_slot(uc); });
         constexpr int gi = SA::group(k);
         if constexpr (gi >= 1) {
           constexpr int G = SA::gsize(gi), jx = k - SA::gstart(gi);
@@ -662,47 +832,60 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       // and the flag is re-polled after the dQ MFMAs only if the turn has not come.
       int seen = rk;
       if (DQM != kDqUnordered && rk > 0 && lane == 0) seen = __hip_atomic_load(flag, __ATOMIC_RELAXED, kFlagScope);
+      // The turn has come once every wave of every earlier contributor has
+      // added: flag >= kWaves * rk. The counter only grows, and a wave of this
+      // workgroup adds only after seeing the turn, so a larger value (a
+      // sibling wave already done) also means the turn has come.
+      const int turn_val = kWaves * rk;
       lds_barrier();  // dS^T complete
       // early: the turn has come already (or this is the first contribution),
       // so the accumulator is read right away and the adds are issued early;
       // the delay injection of the tests always takes the late path
       const bool early = DQM != kDqUnordered &&
-                         (rk == 0 || (a.delay_seed == 0 && __builtin_amdgcn_readfirstlane(seen) == rk));
+                         (rk == 0 || (a.delay_seed == 0 && __builtin_amdgcn_readfirstlane(seen) >= turn_val));
 
-      // ---- stream B: dQ partial = dS K (this wave's D block, MQD row blocks), then dV/dK of the last block ----
-      constexpr int NB1 = C::MQD * C::KKV;
-      constexpr int NB = NB1 + SA::NDK;
+      // ---- stream B: dQ partial = dS K (this wave's DW column blocks x MQD row blocks), then dV/dK of the last block ----
+      using SB_ = StreamB<C>;
+      constexpr int NB1 = SB_::NB1;
+      constexpr int NB = SB_::N;
       // MFMA index before which the RMW adds are issued: early when the reads
       // went out before the dQ MFMAs, later when they wait for the turn
-      constexpr int kAddEarly = NB1 + SA::NDK / 4;
+      constexpr int kAddEarly = NB1 + (SA::NDK * DETATTN_ADD_EARLY) / 8;
       constexpr int kAddLate = NB1 + (3 * SA::NDK) / 4;
-      f32x16 dqAcc[C::MQD];
+      constexpr int NQB = C::MQD * C::DW;  // dQ blocks of this wave: row block m, column block n at m * DW + n
+      f32x16 dqAcc[NQB];
 #pragma unroll
-      for (int m = 0; m < C::MQD; ++m) dqAcc[m] = f32x16{};
-      float old[C::MQD][16];
+      for (int m = 0; m < NQB; ++m) dqAcc[m] = f32x16{};
+      float old[NQB][16];
       // accumulator of dQ tile i: uniform base + 32-bit per-lane byte offset
       unsigned char* dqbase = reinterpret_cast<unsigned char*>(a.dqacc + head_off + qrow0 * D);
 
-      auto loadB = [&](auto kc, Opnd& o) {
-        constexpr int k = decltype(kc)::value;
-        if constexpr (k < NB1) {
-          constexpr int m = k % C::MQD, s = k / C::MQD;
-          o.lo = lds_tr_asm<16 * s * C::PS + 64 * m>(aS);
-          o.hi = lds_tr_asm<(16 * s + 4) * C::PS + 64 * m>(aS);
+      // operand load l (dQ: dS of row block m, K step s; then one per dV/dK MFMA)
+      auto loadB = [&](auto lc, Opnd& o) {
+        constexpr int l = decltype(lc)::value;
+        if constexpr (l < SB_::NL1) {
+          constexpr int m = l % C::MQD, s = l / C::MQD;
+          static_assert(m == 0, "one dS row block per wave");
+          o.lo = lds_tr_asm<16 * s * C::PS>(aS);
+          o.hi = lds_tr_asm<16 * s * C::PS>(aS_hi);
         } else {
-          constexpr int x = k - NB1, kind = 2 + (x & 1), st = x >> 1;
+          constexpr int x = l - SB_::NL1, kind = 2 + (x & 1), st = x >> 1;
           constexpr int sq = 2 * (C::MQ - 1) + st / C::ND, n = st % C::ND;
-          constexpr int off = (kind == 2 ? C::QB : 0) + 16 * sq * C::PD + 64 * n;
-          o.lo = lds_tr_asm<off>(aT);
-          o.hi = lds_tr_asm<off + 8 * C::PD>(aT);
+          if constexpr (C::TCOPY) {
+            o.q = lds_ld16_asm<(kind == 2 ? C::QTB : 0) + 32 * n * C::PT + 32 * sq>(aQT);
+          } else {
+            constexpr int off = (kind == 2 ? C::QB : 0) + 16 * sq * C::PD + 64 * n;
+            o.lo = lds_tr_asm<off>(aT);
+            o.hi = lds_tr_asm<off + 2 * C::PD>(aT);
+          }
         }
       };
       auto mfmaB = [&](auto kc, const u32x4& opr) {
         constexpr int k = decltype(kc)::value;
         const bf16x8 op = as_bf16x8(opr);
         if constexpr (k < NB1) {
-          constexpr int m = k % C::MQD, s = k / C::MQD;
-          dqAcc[m] = mfma32(op, kTB[s], dqAcc[m]);
+          constexpr int l = k / C::DW, n = k % C::DW, m = l % C::MQD, s = l / C::MQD;
+          dqAcc[m * C::DW + n] = mfma32(op, kTB[s * C::DW + n], dqAcc[m * C::DW + n]);
         } else {
           constexpr int x = k - NB1, kind = 2 + (x & 1), st = x >> 1;
           constexpr int sq = 2 * (C::MQ - 1) + st / C::ND, n = st % C::ND;
@@ -711,8 +894,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
         }
       };
       // (uniform row base) + (32-bit lane offset): global accesses with an SGPR base
-      auto dqp = [&](int m, int r) -> float* {
-        unsigned char* row = dqbase + (32 * m + 8 * (r >> 2) + (r & 3)) * D * 4;
+      auto dqp = [&](int mb, int r) -> float* {
+        const int m = mb / C::DW, n = mb % C::DW;
+        unsigned char* row = dqbase + (32 * m + 8 * (r >> 2) + (r & 3)) * D * 4 + 32 * n * 4;
         return reinterpret_cast<float*>(row + (size_t)(uint32_t)dqlane);
       };
 
@@ -723,10 +907,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
             const long long until = now_ticks() + (hash3(a.delay_seed, (unsigned)gidx, (unsigned)(t * 4 + w)) & 1023u);
             while (now_ticks() < until) __builtin_amdgcn_s_sleep(2);
           }
-          if (seen != rk) {
+          if (seen < turn_val) {
             const long long t0 = now_ticks();
             int spins = 0;
-            while (__hip_atomic_load(flag, __ATOMIC_RELAXED, kFlagScope) != rk) {
+            while (__hip_atomic_load(flag, __ATOMIC_RELAXED, kFlagScope) < turn_val) {
               __builtin_amdgcn_s_sleep(1);
               if (((++spins) & 255) == 0) {
                 if (now_ticks() - t0 > a.timeout_ticks ||
@@ -745,12 +929,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
         if (rk > 0) {
           if constexpr (DQM == kDqLocalRmw) asm volatile("buffer_inv sc0" ::: "memory");
 #pragma unroll
-          for (int m = 0; m < C::MQD; ++m)
+          for (int m = 0; m < NQB; ++m)
 #pragma unroll
             for (int r = 0; r < 16; ++r) old[m][r] = __hip_atomic_load(dqp(m, r), __ATOMIC_RELAXED, kScope);
         } else {
 #pragma unroll
-          for (int m = 0; m < C::MQD; ++m)
+          for (int m = 0; m < NQB; ++m)
 #pragma unroll
             for (int r = 0; r < 16; ++r) old[m][r] = 0.f;
         }
@@ -761,7 +945,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       auto adds_begin = [&]() {
         if constexpr (DQM == kDqUnordered) {
 #pragma unroll
-          for (int m = 0; m < C::MQD; ++m)
+          for (int m = 0; m < NQB; ++m)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
               __hip_atomic_fetch_add(dqp(m, r), dqAcc[m][r], __ATOMIC_RELAXED,
@@ -775,13 +959,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
           if constexpr (!kRmw) {  // ordered atomic adds; the first contributor stores
             if (rk == 0) {
 #pragma unroll
-              for (int m = 0; m < C::MQD; ++m)
+              for (int m = 0; m < NQB; ++m)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                   __hip_atomic_store(dqp(m, r), dqAcc[m][r], __ATOMIC_RELAXED, kScope);
             } else {
 #pragma unroll
-              for (int m = 0; m < C::MQD; ++m)
+              for (int m = 0; m < NQB; ++m)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                   __hip_atomic_fetch_add(dqp(m, r), dqAcc[m][r], __ATOMIC_RELAXED,
@@ -794,28 +978,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       auto adds_finish = [&]() {
         if constexpr (kRmw) {
 #pragma unroll
-          for (int m = 0; m < C::MQD; ++m)
+          for (int m = 0; m < NQB; ++m)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
               __hip_atomic_store(dqp(m, r), old[m][r] + dqAcc[m][r], __ATOMIC_RELAXED,
                                  kScope);
           __atomic_signal_fence(__ATOMIC_SEQ_CST);
         }
-        if constexpr (DQM != kDqUnordered) {
-          const bool withhold = (a.skip_item >= 0 && gidx == a.skip_item && t == 0);
-          pend_flag = withhold ? nullptr : flag;
-          pend_val = rk + 1;
-        }
         trace_rec(4, t, gidx);
-        // Prefetch tile t+2 into the buffer tile t-1 used. Issued after the
-        // adds, so waiting for the adds (next tile top) or for later loads
-        // never waits for this DMA.
-        dma_pending = t + 2 < t_end;
-        if (dma_pending) {
-          int ni, nj;
-          sc.tile(it, t + 2, ni, nj);
-          dma_q(b == 0 ? 2 : b - 1, head_off, bhS, ni);
-        }
       };
 
       if constexpr (kRmw) {
@@ -824,7 +994,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
           rmw_loads();
         }
       }
-      static_for<0, PF>([&](auto kc) { loadB(kc, ring[decltype(kc)::value]); });
+      static_for<0, PF>([&](auto lc) { loadB(lc, ring[decltype(lc)::value]); });
       static_for<0, NB>([&](auto kc) {
         constexpr int k = decltype(kc)::value;
         if constexpr (k == NB1) {
@@ -841,38 +1011,41 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
           if (!kRmw || !early) adds_finish();
           DETATTN_FENCE();
         }
-        if constexpr (k + PF < NB) loadB(std::integral_constant<int, k + PF>{}, ring[(k + PF) % RING]);
-        Opnd& o = ring[k % RING];
-        lgkm_wait<2 * (k + PF < NB ? PF : NB - 1 - k)>(o.lo, o.hi);  // two reads per operand
-        mfmaB(kc, cat2(o.lo, o.hi));
+        // loads that may be issued now (pf loads ahead of this MFMA's own)
+        constexpr int l0 = k == 0 ? PF : SB_::issued_by(k - 1, PF) + 1, l1 = SB_::issued_by(k, PF);
+        static_for<l0, l1 + 1>([&](auto lc) { loadB(lc, ring[decltype(lc)::value % RING]); });
+        constexpr int l = SB_::load_of(k);
+        Opnd& o = ring[l % RING];
+        if constexpr (k >= NB1 && C::TCOPY) {
+          lgkm_wait<SB_::insts_after(k, PF)>(o.q);
+          mfmaB(kc, o.q);
+        } else {
+          if constexpr (SB_::first_use(k)) lgkm_wait<SB_::insts_after(k, PF)>(o.lo, o.hi);
+          mfmaB(kc, cat2(o.lo, o.hi));
+        }
         DETATTN_FENCE();
       });
 
       trace_rec(5, t, gidx);
+      // This wave's adds (and the next tile's DMA, issued earlier) are
+      // complete: publish the wave's share of the contribution right away.
+      // The flag counts wave contributions, so no barrier sits between the
+      // adds and the hand-off to the next contributor.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if constexpr (DQM != kDqUnordered) {
+        const bool withhold = (a.skip_item >= 0 && gidx == a.skip_item && t == 0);
+        if (lane == 0 && !withhold) __hip_atomic_fetch_add(flag, 1, __ATOMIC_RELAXED, kFlagScope);
+      }
       ++t;
       if (t >= t_end) break;
-      b = b == 2 ? 0 : b + 1;
-      // The next tile's DMA (issued during the previous tile) and this tile's
-      // accumulator adds are complete in every wave; the DMA issued during
-      // this tile (the newest vector-memory operations) may stay in flight.
-      if (dma_pending) {
-        if (w == 0) vm_barrier<C::dma_ops(0)>();
-        else if (w == 1) vm_barrier<C::dma_ops(1)>();
-        else if (w == 2) vm_barrier<C::dma_ops(2)>();
-        else vm_barrier<C::dma_ops(3)>();
-      } else {
-        vm_barrier<0>();
-      }
-      if (tid == 0 && pend_flag) __hip_atomic_store(pend_flag, pend_val, __ATOMIC_RELAXED, kFlagScope);
-      pend_flag = nullptr;
+      b = nb;
+      lds_barrier();  // the next tile's data is in LDS in every wave's share
     } while (true);  // tiles of the segment
 
-    // ---- end of a column: publish, then dK, dV of KV tile j to global ----
+    // ---- end of a column: dK, dV of KV tile j to global ----
     mfma_agpr_drain();
     wait_vm_all();
     __syncthreads();
-    if (tid == 0 && pend_flag) __hip_atomic_store(pend_flag, pend_val, __ATOMIC_RELAXED, kFlagScope);
-    pend_flag = nullptr;
     {
       float* red = reinterpret_cast<float*>(smem);
       __bf16* sOut = reinterpret_cast<__bf16*>(smem + C::RED_BYTES);

@@ -21,6 +21,7 @@ struct MainInfo {
   const void* func;  // kernel symbol, or nullptr if the combination is not built
   int lds_bytes;
   int occupancy;     // workgroups per compute unit (0 if unknown)
+  int tcopy;         // the instance reads the transposed Q, dO copies (bwd_transpose_kernel)
 };
 
 MainInfo main_info_d64(int BQ, int BKV, int causal, int dq_mode);
@@ -30,6 +31,8 @@ hipError_t launch_pre(int D, const __bf16* o, const __bf16* dout, const float* l
                       float* ndelta,
                       long long rows, int* flags,
                       long long n_flags, unsigned* header, float* dqacc, long long dqacc_elems, hipStream_t st);
+hipError_t launch_transpose(int D, const __bf16* q, const __bf16* dout, __bf16* qt, __bf16* dot, long long BH, int S,
+                            hipStream_t st);
 hipError_t launch_convert(const float* acc, __bf16* dq, long long elems, float scale, hipStream_t st);
 hipError_t launch_main(const MainLaunch& L, hipStream_t st);
 hipError_t launch_fwd(int D, int causal, const __bf16* q, const __bf16* k, const __bf16* v, __bf16* o, float* lse,

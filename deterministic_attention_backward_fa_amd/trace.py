@@ -57,7 +57,27 @@ def summarize(recs):
             for a, b, name in INTERVALS:
                 if ph[x] == a and ph[x + 1] == b:
                     sums[name].append(t[x + 1] - t[x])
-    out = {name: (float(np.mean(v)) if v else 0.0) for name, v in sums.items()}
+    # mean ticks per tile: each interval's total over all tiles (intervals of
+    # only one of the two turn paths are weighted by how often that path runs)
+    n_tiles = max(1, sum(len(v) for a, b, v in ((a, b, sums[n]) for a, b, n in INTERVALS) if (a, b) == (0, 1)))
+    out = {name: (float(np.sum(v)) / n_tiles if v else 0.0) for name, v in sums.items()}
     total = sum(out.values())
+    # tile period (top to top) and how many tiles found their turn already come
+    # at the dS^T barrier (turn recorded before the dQ MFMAs)
+    periods, early, late = [], 0, 0
+    for wg in range(recs.shape[0]):
+        r = recs[wg]
+        r = r[r[:, 0] != 0]
+        t = r[:, 0].astype(np.int64)
+        ph = (r[:, 1] & 0xFF).astype(np.int64)
+        tops = t[ph == 0]
+        if len(tops) > 1:
+            periods.extend(np.diff(tops).tolist())
+        for x in range(len(r) - 1):
+            if ph[x] == 1:
+                early += int(ph[x + 1] == 3)
+                late += int(ph[x + 1] == 2)
     return {"mean_ticks_per_tile": total, "share": {k: (v / total if total else 0.0) for k, v in out.items()},
-            "ticks": out, "workgroups": len(spans)}
+            "ticks": out, "workgroups": len(spans),
+            "tile_period_median": float(np.median(periods)) if periods else 0.0,
+            "early_turn_fraction": early / (early + late) if early + late else 0.0}
