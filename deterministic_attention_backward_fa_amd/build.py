@@ -18,10 +18,11 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdetattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["capi.cpp", "kernels_misc.hip", "bwd_d64.hip", "bwd_d128.hip"]
+MAIN_SOURCES = ["bwd_d64.hip", "bwd_d128.hip", "bwd_d64_trace.hip", "bwd_d128_trace.hip"]
+SOURCES = ["capi.cpp", "kernels_misc.hip"] + MAIN_SOURCES
 # The main backward kernel keeps MFMA results the VALU reads in VGPRs (its
 # AGPR-resident accumulations are written as explicit AGPR-form MFMAs).
-PER_SOURCE = {"bwd_d64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "bwd_d128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+PER_SOURCE = {src: ["-mllvm", "-amdgpu-mfma-vgpr-form"] for src in MAIN_SOURCES}
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 instructions.
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",

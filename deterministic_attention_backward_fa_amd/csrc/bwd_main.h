@@ -412,7 +412,7 @@ __device__ __forceinline__ void dma16(const void* gsrc, void* lds) {
   __builtin_amdgcn_global_load_lds((gbl_void*)gsrc, (lds_void*)lds, 16, 0, 0);
 }
 
-template <int D, int BQ, int BKV, bool CAUSAL, int DQM>
+template <int D, int BQ, int BKV, bool CAUSAL, int DQM, bool TRACE>
 __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   using C = MainCfg<D, BQ, BKV>;
   using SA = StreamA<C>;
@@ -465,7 +465,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   const int oW = C::OFF_DS + w_row * C::PS + 8 * g;
   const int oL = C::OFF_LD + (C::QW * wq + 4 * g) * 4;                           // row terms (buffer-relative)
   const int oQT = C::OFF_QT + c32 * C::PT + g * 16 + C::QW * wq * 2;              // Q^T, dO^T fragments (TCOPY)
-  const int dqlane = ((32 * mq0 + 4 * g) * D + 32 * nbq + c32) * 4;  // dQ accumulator tile, per lane
+  // dQ accumulator, fragment order: 32 x 32 blocks of 4 KB; inside a block,
+  // register group h (rows 8h + 4g .. + 3, column lane%32) of every lane is
+  // one 1 KB run, lane-major, 16 bytes per lane. A wave's block mb starts at
+  // byte dqblk(mb) of the Q tile.
+  constexpr int NQB = C::MQD * C::DW;  // dQ blocks of this wave: row block m, column block n at m * DW + n
+  auto dqblk = [&](int mb) -> int { return ((mq0 + mb / C::DW) * C::ND + nbq + mb % C::DW) * 4096; };
+  int dqlane[NQB];
+#pragma unroll
+  for (int mb = 0; mb < NQB; ++mb) dqlane[mb] = dqblk(mb) + lane * 16;
   int goffQ[C::DMA_QW];
 #pragma unroll
   for (int x = 0; x < C::DMA_QW; ++x) goffQ[x] = dma_goff<C::NCH>(w + 4 * x, lane);
@@ -547,11 +555,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   // Optional phase trace: wave 0, lane 0 of each workgroup.
   int trace_n = 0;
   auto trace_rec = [&](int phase, int t, long long item) {
-    if (a.trace && tid == 0 && trace_n < a.trace_records) {
-      unsigned long long* p = a.trace + ((size_t)blockIdx.x * a.trace_records + trace_n) * 2;
-      p[0] = __builtin_amdgcn_s_memtime();
-      p[1] = (unsigned long long)phase | ((unsigned long long)(t & 0xFFFFFF) << 8) | ((unsigned long long)item << 32);
-      ++trace_n;
+    if constexpr (TRACE) {
+      if (tid == 0 && trace_n < a.trace_records) {
+        unsigned long long* p = a.trace + ((size_t)blockIdx.x * a.trace_records + trace_n) * 2;
+        p[0] = __builtin_amdgcn_s_memtime();
+        p[1] = (unsigned long long)phase | ((unsigned long long)(t & 0xFFFFFF) << 8) | ((unsigned long long)item << 32);
+        ++trace_n;
+      }
     }
   };
 
@@ -572,12 +582,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     const int it = (int)(gidx % ipH);
     const long long head_off = (long long)bh * a.S * D;
     const long long bhS = (long long)bh * a.S;
+    // the head's dQ accumulator as a buffer resource (32-bit offsets, range-checked)
+    const __amdgpu_buffer_rsrc_t dqrsrc =
+        __builtin_amdgcn_make_buffer_rsrc(a.dqacc + head_off, 0, a.S * D * 4, kBufferWord3);
 
 
     for (int seg = 0; seg < sc.segments(); ++seg) {
     const int t_begin = sc.seg_begin(it, seg), t_end = sc.seg_end(it, seg);
-    int i0, j;
-    sc.tile(it, t_begin, i0, j);
+    int j;
+    SegWalk cur = sc.walk(it, seg, j);  // at step t_begin
+    const int i0 = cur.i;
     // ---- segment prologue: K_j, V_j and the first Q tile, synchronously ----
     {
       const unsigned char* gk = reinterpret_cast<const unsigned char*>(a.k + head_off + (long long)j * BKV * D);
@@ -653,8 +667,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     int t = t_begin;
     int b = 0;  // buffer of tile t
     do {
-      int i, jj;
-      sc.tile(it, t, i, jj);
+      const int i = cur.i;
       const int nb = b + 1 == C::NBUF ? 0 : b + 1;  // buffer of tile t+1
       const long long qrow0 = (long long)i * BQ;
       trace_rec(0, t, gidx);
@@ -663,12 +676,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       // fewer instructions than others repeats its tile's last instruction,
       // and in the last tile of a column the current tile is loaded again
       // into the idle buffer (the same bytes, or bytes no one reads).
-      int ni = i;
-      if (t + 1 < t_end) {
-        int nj;
-        sc.tile(it, t + 1, ni, nj);
-      }
-      ni = __builtin_amdgcn_readfirstlane(ni);
+      SegWalk nxt = cur;
+      if (t + 1 < t_end) nxt.advance(t + 1);
+      const int ni = __builtin_amdgcn_readfirstlane(nxt.i);
       const long long nrow0 = (long long)ni * BQ;
       unsigned char* nbase = smem + C::OFF_B0 + nb * C::BUF;
       auto dma_slot = [&](auto uc) {
@@ -697,7 +707,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
         }
       };
       // this tile's turn in dQ tile i's order: rank rk; the flag counts the wave contributions added
-      const int rk = DQM == kDqUnordered ? 0 : sc.rank(i, j);
+      const int rk = DQM == kDqUnordered ? 0 : cur.rank_now();
       int* flag = a.flags + ((long long)bh * sc.n_q + i) * kFlagInts;
       const int vb = C::OFF_B0 + b * C::BUF;
       const int vL = oL + vb;
@@ -852,13 +862,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       // went out before the dQ MFMAs, later when they wait for the turn
       constexpr int kAddEarly = NB1 + (SA::NDK * DETATTN_ADD_EARLY) / 8;
       constexpr int kAddLate = NB1 + (3 * SA::NDK) / 4;
-      constexpr int NQB = C::MQD * C::DW;  // dQ blocks of this wave: row block m, column block n at m * DW + n
       f32x16 dqAcc[NQB];
 #pragma unroll
       for (int m = 0; m < NQB; ++m) dqAcc[m] = f32x16{};
-      float old[NQB][16];
-      // accumulator of dQ tile i: uniform base + 32-bit per-lane byte offset
-      unsigned char* dqbase = reinterpret_cast<unsigned char*>(a.dqacc + head_off + qrow0 * D);
+      f32x4 old[NQB][4];
+      // dQ tile i in the head's accumulator: uniform byte offset (buffer accesses)
+      const int dqtile = (int)(qrow0 * D * 4);
+      unsigned char* dqbase = reinterpret_cast<unsigned char*>(a.dqacc + head_off) + dqtile;
 
       // operand load l (dQ: dS of row block m, K step s; then one per dV/dK MFMA)
       auto loadB = [&](auto lc, Opnd& o) {
@@ -893,11 +903,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
           else mfma_agpr(dKacc[n], dsB[sq], opr);
         }
       };
-      // (uniform row base) + (32-bit lane offset): global accesses with an SGPR base
+      // element r of block mb (atomic modes): (uniform tile base) + (32-bit lane offset)
       auto dqp = [&](int mb, int r) -> float* {
-        const int m = mb / C::DW, n = mb % C::DW;
-        unsigned char* row = dqbase + (32 * m + 8 * (r >> 2) + (r & 3)) * D * 4 + 32 * n * 4;
-        return reinterpret_cast<float*>(row + (size_t)(uint32_t)dqlane);
+        return reinterpret_cast<float*>(dqbase + (uint32_t)(dqlane[mb] + (r >> 2) * 1024 + (r & 3) * 4));
+      };
+      // register group h of block mb: one 16-byte access per lane, cache scope of the mode
+      constexpr int kAux = kScope == __HIP_MEMORY_SCOPE_WORKGROUP ? kBufSc0 : kBufSc1;
+      auto dq_load4 = [&](int mb, int h) -> f32x4 {
+        return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(dqrsrc, dqlane[mb] + h * 1024, dqtile, kAux));
+      };
+      auto dq_store4 = [&](int mb, int h, f32x4 v) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), dqrsrc, dqlane[mb] + h * 1024, dqtile, kAux);
+      };
+      auto acc4 = [&](int mb, int h) -> f32x4 {
+        return f32x4{dqAcc[mb][4 * h], dqAcc[mb][4 * h + 1], dqAcc[mb][4 * h + 2], dqAcc[mb][4 * h + 3]};
       };
 
       // wait for the turn of this workgroup's partial in dQ tile i's order
@@ -931,12 +950,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
           for (int m = 0; m < NQB; ++m)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) old[m][r] = __hip_atomic_load(dqp(m, r), __ATOMIC_RELAXED, kScope);
+            for (int h = 0; h < 4; ++h) old[m][h] = dq_load4(m, h);
         } else {
 #pragma unroll
           for (int m = 0; m < NQB; ++m)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) old[m][r] = 0.f;
+            for (int h = 0; h < 4; ++h) old[m][h] = f32x4{};
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
       };
@@ -961,8 +980,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
               for (int m = 0; m < NQB; ++m)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                  __hip_atomic_store(dqp(m, r), dqAcc[m][r], __ATOMIC_RELAXED, kScope);
+                for (int h = 0; h < 4; ++h) dq_store4(m, h, acc4(m, h));
             } else {
 #pragma unroll
               for (int m = 0; m < NQB; ++m)
@@ -980,9 +998,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
           for (int m = 0; m < NQB; ++m)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              __hip_atomic_store(dqp(m, r), old[m][r] + dqAcc[m][r], __ATOMIC_RELAXED,
-                                 kScope);
+            for (int h = 0; h < 4; ++h) dq_store4(m, h, old[m][h] + acc4(m, h));
           __atomic_signal_fence(__ATOMIC_SEQ_CST);
         }
         trace_rec(4, t, gidx);
@@ -1038,6 +1054,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       }
       ++t;
       if (t >= t_end) break;
+      cur = nxt;
       b = nb;
       lds_barrier();  // the next tile's data is in LDS in every wave's share
     } while (true);  // tiles of the segment

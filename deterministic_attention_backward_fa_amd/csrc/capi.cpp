@@ -90,8 +90,7 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
 
   // The kernel instance depends on the dQ mode, which depends on the ring
   // placement below; occupancy (LDS-bound) is the same for every mode.
-  const MainInfo info0 = s.D == 64 ? main_info_d64(bq, bkv, causal, kDqOrderedRmw)
-                                   : main_info_d128(bq, bkv, causal, kDqOrderedRmw);
+  const MainInfo info0 = main_info(s.D, bq, bkv, causal, kDqOrderedRmw, false);
   if (!info0.func) return DETATTN_ERR_UNSUPPORTED;
 
   const Sched sc{(int)sch, causal, n_q, n_kv, r};
@@ -142,7 +141,7 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
           : pub_dqm == DETATTN_DQ_XCD_LOCAL_RMW ? kDqLocalRmw
                                                  : kDqOrderedRmw;
   }
-  const MainInfo info = s.D == 64 ? main_info_d64(bq, bkv, causal, dqm) : main_info_d128(bq, bkv, causal, dqm);
+  const MainInfo info = main_info(s.D, bq, bkv, causal, dqm, false);
   if (!info.func) return DETATTN_ERR_UNSUPPORTED;
   P.pub.block_q = bq;
   P.pub.block_kv = bkv;
@@ -236,8 +235,7 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
   __bf16* qt = reinterpret_cast<__bf16*>(ws + L.qt_off);
   __bf16* dot = reinterpret_cast<__bf16*>(ws + L.dot_off);
   {
-    const MainInfo info = s.D == 64 ? main_info_d64(P.pub.block_q, P.pub.block_kv, P.causal, P.dqm_internal)
-                                    : main_info_d128(P.pub.block_q, P.pub.block_kv, P.causal, P.dqm_internal);
+    const MainInfo info = main_info(s.D, P.pub.block_q, P.pub.block_kv, P.causal, P.dqm_internal, false);
     if (info.tcopy) {
       e = launch_transpose(s.D, static_cast<const __bf16*>(q), static_cast<const __bf16*>(dout), qt, dot, BH, s.S, st_);
       if (e != hipSuccess) return DETATTN_ERR_HIP;
@@ -293,7 +291,7 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
     (void)hipGetLastError();
     return e == hipErrorCooperativeLaunchTooLarge ? DETATTN_ERR_UNSUPPORTED : DETATTN_ERR_HIP;
   }
-  e = launch_convert(dqacc, static_cast<__bf16*>(dq), elems, s.softmax_scale, st_);
+  e = launch_convert(s.D, dqacc, static_cast<__bf16*>(dq), rows, s.softmax_scale, st_);
   return e == hipSuccess ? DETATTN_OK : DETATTN_ERR_HIP;
 }
 
@@ -345,12 +343,22 @@ int detattn_schedule_item(int32_t schedule, int32_t mask, int32_t n_q, int32_t n
   if (ip < 0 || item < 0 || item >= ip || cap < 0) return -1;
   const Sched sc{schedule, mask, n_q, n_kv, n_q / n_kv};
   const int len = sc.item_len(item);
-  for (int t = 0; t < len && t < cap; ++t) {
-    int i, j;
-    sc.tile(item, t, i, j);
-    if (q_tiles) q_tiles[t] = i;
-    if (kv_tiles) kv_tiles[t] = j;
-    if (ranks) ranks[t] = schedule == kAtomicNondet ? -1 : sc.rank(i, j);
+  // the incremental walk the device takes, checked step by step against the
+  // closed forms tile() and rank()
+  for (int seg = 0; seg < sc.segments(); ++seg) {
+    int j;
+    SegWalk wk = sc.walk(item, seg, j);
+    for (int t = sc.seg_begin(item, seg); t < sc.seg_end(item, seg); ++t) {
+      if (t > sc.seg_begin(item, seg)) wk.advance(t);
+      int ci, cj;
+      sc.tile(item, t, ci, cj);
+      if (ci != wk.i || cj != j || (schedule != kAtomicNondet && sc.rank(ci, cj) != wk.rank_now())) return -2;
+      if (t < cap) {
+        if (q_tiles) q_tiles[t] = wk.i;
+        if (kv_tiles) kv_tiles[t] = j;
+        if (ranks) ranks[t] = schedule == kAtomicNondet ? -1 : wk.rank_now();
+      }
+    }
   }
   return len;
 }

@@ -5,23 +5,33 @@
 
 namespace detattn {
 
-// dQ = bf16_rne(scale * acc), 8 elements per thread.
+// dQ = bf16_rne(scale * acc). The accumulator is in fragment order
+// (dqacc_index): a workgroup takes 32-row blocks, reads each block's 16-byte
+// runs, and writes the rows through LDS as 16-byte runs.
+template <int D>
 __global__ __launch_bounds__(256) void bwd_convert_kernel(const float* __restrict__ acc, __bf16* __restrict__ dq,
-                                                          long long n8, float scale) {
-  const long long gsz = (long long)gridDim.x * 256;
-  for (long long x = (long long)blockIdx.x * 256 + threadIdx.x; x < n8; x += gsz) {
-    const f32x4 a = reinterpret_cast<const f32x4*>(acc)[2 * x];
-    const f32x4 b = reinterpret_cast<const f32x4*>(acc)[2 * x + 1];
-    bf16x8 r;
+                                                          long long row_blocks, float scale) {
+  constexpr int PITCH = D + 8;          // bf16 per LDS row (16-byte aligned rows)
+  constexpr int RUNS_IN = D / 32 * 256;  // 16-byte accumulator runs per row block
+  __shared__ __attribute__((aligned(16))) __bf16 tile[32 * PITCH];
+  for (long long rb = blockIdx.x; rb < row_blocks; rb += gridDim.x) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(acc + rb * 32 * D);
+    for (int c = threadIdx.x; c < RUNS_IN; c += 256) {
+      const f32x4 v = src[c];
+      // run c: column block c / 256, register group h, lane (g, column c % 32)
+      const int h = (c >> 6) & 3, ln = c & 63;
+      const int row = 8 * h + 4 * (ln >> 5), col = (c >> 8) * 32 + (ln & 31);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      r[t] = (__bf16)(scale * a[t]);
-      r[4 + t] = (__bf16)(scale * b[t]);
+      for (int e = 0; e < 4; ++e) tile[(row + e) * PITCH + col] = (__bf16)(scale * v[e]);
     }
-    reinterpret_cast<bf16x8*>(dq)[x] = r;
+    __syncthreads();
+    for (int x = threadIdx.x; x < 32 * D / 8; x += 256) {
+      const int row = x / (D / 8), c8 = x % (D / 8);
+      reinterpret_cast<bf16x8*>(dq + (rb * 32 + row) * D)[c8] = *reinterpret_cast<const bf16x8*>(tile + row * PITCH + c8 * 8);
+    }
+    __syncthreads();
   }
 }
-
 
 static int grid_for(long long work_items, int per_block, int cap) {
   long long g = (work_items + per_block - 1) / per_block;
@@ -57,16 +67,18 @@ hipError_t launch_transpose(int D, const __bf16* q, const __bf16* dout, __bf16* 
   return hipGetLastError();
 }
 
-hipError_t launch_convert(const float* acc, __bf16* dq, long long elems, float scale, hipStream_t st) {
-  const long long n8 = elems / 8;
-  const int g = grid_for(n8, 256, 256 * 16);
-  bwd_convert_kernel<<<dim3(g), dim3(256), 0, st>>>(acc, dq, n8, scale);
+hipError_t launch_convert(int D, const float* acc, __bf16* dq, long long rows, float scale, hipStream_t st) {
+  const long long rb = rows / 32;
+  const int g = grid_for(rb, 1, 256 * 16);
+  if (D == 64)
+    bwd_convert_kernel<64><<<dim3(g), dim3(256), 0, st>>>(acc, dq, rb, scale);
+  else
+    bwd_convert_kernel<128><<<dim3(g), dim3(256), 0, st>>>(acc, dq, rb, scale);
   return hipGetLastError();
 }
 
 hipError_t launch_main(const MainLaunch& L, hipStream_t st) {
-  MainInfo info = L.D == 64 ? main_info_d64(L.BQ, L.BKV, L.causal, L.dq_mode)
-                            : main_info_d128(L.BQ, L.BKV, L.causal, L.dq_mode);
+  MainInfo info = main_info(L.D, L.BQ, L.BKV, L.causal, L.dq_mode, L.args.trace != nullptr);
   if (!info.func) return hipErrorInvalidDeviceFunction;
   BwdArgs args = L.args;
   void* kargs[] = {(void*)&args};

@@ -26,6 +26,16 @@ struct MainInfo {
 
 MainInfo main_info_d64(int BQ, int BKV, int causal, int dq_mode);
 MainInfo main_info_d128(int BQ, int BKV, int causal, int dq_mode);
+MainInfo main_info_d64_trace(int BQ, int BKV, int causal, int dq_mode);
+MainInfo main_info_d128_trace(int BQ, int BKV, int causal, int dq_mode);
+
+// The instance for head dimension D (64 or 128); `trace` selects the variant
+// that writes the per-tile phase trace.
+inline MainInfo main_info(int D, int BQ, int BKV, int causal, int dq_mode, bool trace) {
+  if (D == 64) return trace ? main_info_d64_trace(BQ, BKV, causal, dq_mode) : main_info_d64(BQ, BKV, causal, dq_mode);
+  if (D == 128) return trace ? main_info_d128_trace(BQ, BKV, causal, dq_mode) : main_info_d128(BQ, BKV, causal, dq_mode);
+  return MainInfo{nullptr, 0, 0, 0};
+}
 
 hipError_t launch_pre(int D, const __bf16* o, const __bf16* dout, const float* lse, float inv_scale, float* nlse,
                       float* ndelta,
@@ -33,7 +43,7 @@ hipError_t launch_pre(int D, const __bf16* o, const __bf16* dout, const float* l
                       long long n_flags, unsigned* header, float* dqacc, long long dqacc_elems, hipStream_t st);
 hipError_t launch_transpose(int D, const __bf16* q, const __bf16* dout, __bf16* qt, __bf16* dot, long long BH, int S,
                             hipStream_t st);
-hipError_t launch_convert(const float* acc, __bf16* dq, long long elems, float scale, hipStream_t st);
+hipError_t launch_convert(int D, const float* acc, __bf16* dq, long long rows, float scale, hipStream_t st);
 hipError_t launch_main(const MainLaunch& L, hipStream_t st);
 hipError_t launch_fwd(int D, int causal, const __bf16* q, const __bf16* k, const __bf16* v, __bf16* o, float* lse,
                       int BH, int S, float scale, hipStream_t st);

@@ -26,6 +26,40 @@
 
 namespace detattn {
 
+// Incremental walk over one segment of an item: the Q tile and rank of each
+// step from the previous step's with a few integer operations, so a kernel's
+// per-tile bookkeeping needs no division. Sched::walk positions a walk at
+// the segment's first step; advance(t) moves it to step t (the next one).
+// Every schedule's segment is an arithmetic run of Q tiles with at most one
+// wrap-around and at most one jump, and its ranks are either the KV tile
+// itself or a step counter divided by r (shift orders).
+struct SegWalk {
+  int i;                // Q tile of the current step
+  int rank;             // rank of the current step (when ranked by step)
+  int cnt;              // steps taken in the current group of r steps
+  int di;               // Q tile increment per step (+1 or -1)
+  int wrap_at, wrap_to; // a step reaching Q tile wrap_at continues at wrap_to
+  int jump_t, jump_i;   // step jump_t continues at Q tile jump_i, ranks restart at 0
+  int r;                // steps per rank (shift orders)
+  int fixed_rank;       // the rank of every step, or -1 when ranked by step
+
+  __host__ __device__ __forceinline__ int rank_now() const { return fixed_rank >= 0 ? fixed_rank : rank; }
+
+  __host__ __device__ __forceinline__ void advance(int t) {
+    i += di;
+    if (i == wrap_at) i = wrap_to;
+    ++cnt;
+    const bool next_group = cnt == r;
+    cnt = next_group ? 0 : cnt;
+    rank += next_group ? 1 : 0;
+    if (t == jump_t) {
+      i = jump_i;
+      rank = 0;
+      cnt = 0;
+    }
+  }
+};
+
 enum Schedule : int { kSerialAscending = 0, kDescendingQ = 1, kShift = 2, kSymmetricShift = 3, kAtomicNondet = 4 };
 
 struct Sched {
@@ -89,6 +123,60 @@ struct Sched {
         i = (causal ? it * r : 0) + t;
         return;
     }
+  }
+
+  // Walk over segment `seg` of item `it`, at step seg_begin(it, seg); j is the
+  // segment's KV tile. Equal, step by step, to tile() and rank().
+  __host__ __device__ __forceinline__ SegWalk walk(int it, int seg, int& j) const {
+    SegWalk w;
+    w.rank = 0;
+    w.cnt = 0;
+    w.di = 1;
+    w.wrap_at = n_q + 1;  // not reached
+    w.wrap_to = 0;
+    w.jump_t = -1;        // no jump
+    w.jump_i = 0;
+    w.r = r;
+    w.fixed_rank = -1;
+    switch (sch) {
+      case kShift:
+        j = it;
+        w.i = (it * r) % n_q;
+        w.wrap_at = n_q;
+        w.wrap_to = 0;
+        break;
+      case kSymmetricShift: {
+        const int half = n_q / 2;
+        if (seg == 0) {  // phase 1 over rows half.., then column it upward from row it*r
+          j = it;
+          w.i = half + (it * r) % half;
+          w.wrap_at = n_q;
+          w.wrap_to = half;
+          w.jump_t = half;
+          w.jump_i = it * r;
+        } else {         // column n_kv-1-it downward from the last row
+          j = n_kv - 1 - it;
+          w.i = n_q - 1;
+          w.di = -1;
+          w.wrap_at = -2;
+          w.fixed_rank = j;
+        }
+        break;
+      }
+      case kDescendingQ:
+        j = it;
+        w.i = n_q - 1;
+        w.di = -1;
+        w.wrap_at = -2;
+        w.fixed_rank = j;
+        break;
+      default:  // serial ascending, atomic
+        j = it;
+        w.i = causal ? it * r : 0;
+        w.fixed_rank = j;
+        break;
+    }
+    return w;
   }
 
   // Position of KV tile j in dQ tile i's accumulation order.

@@ -192,7 +192,9 @@ const char* detattn_status_string(int status);
  * For item `item` (a KV tile, or a symmetric pair index) of one head with
  * n_q Q tiles and n_kv KV tiles: writes up to `cap` entries of its visit
  * sequence (Q tile, KV tile, rank of that KV tile in the dQ tile's order) and
- * returns the item's length, or -1 on invalid arguments.
+ * returns the item's length, or -1 on invalid arguments. The entries come from
+ * the incremental walk the main kernel takes, checked step by step against the
+ * closed-form definitions; -2 reports a disagreement (an internal error).
  */
 int detattn_schedule_item(int32_t schedule, int32_t mask, int32_t n_q, int32_t n_kv, int32_t item,
                           int32_t* q_tiles, int32_t* kv_tiles, int32_t* ranks, int32_t cap);
