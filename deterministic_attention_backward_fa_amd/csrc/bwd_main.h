@@ -55,7 +55,12 @@
 //   PF         LDS operand loads run this many operands ahead of their MFMA
 //   ELEM_DELAY MFMAs of a group issued before its first elementwise unit
 //   DMA_SPAN   the next tile's DMA is spread over this fraction (1/8ths) of stream A
-//   ADD_EARLY  dV/dK MFMAs (1/8ths of them) issued before the early accumulator adds
+//   PUB_AT     stream-A MFMA of the next tile before which a wave publishes its
+//              previous tile's dQ contribution
+//   LD_SPAN    the dQ accumulator reads are spread over this fraction (1/8ths)
+//              of the dQ MFMAs (0: all before the first)
+//   ST_AT, ST_SPAN  the accumulator writes start after this fraction (1/8ths)
+//              of the dV/dK MFMAs of stream B and are spread over ST_SPAN 1/8ths
 #ifndef DETATTN_PF
 #define DETATTN_PF 4
 #endif
@@ -65,8 +70,17 @@
 #ifndef DETATTN_DMA_SPAN
 #define DETATTN_DMA_SPAN 4
 #endif
-#ifndef DETATTN_ADD_EARLY
-#define DETATTN_ADD_EARLY 2
+#ifndef DETATTN_PUB_AT
+#define DETATTN_PUB_AT 4
+#endif
+#ifndef DETATTN_LD_SPAN
+#define DETATTN_LD_SPAN 0
+#endif
+#ifndef DETATTN_ST_AT
+#define DETATTN_ST_AT 0
+#endif
+#ifndef DETATTN_ST_SPAN
+#define DETATTN_ST_SPAN 4
 #endif
 
 namespace detattn {
@@ -112,7 +126,11 @@ struct MainCfg {
   // (when LDS allows) gives K_j, V_j room to be staged at the start of a
   // column next to the first Q tile
   static constexpr int NBUF = TCOPY ? 2 : 3;
-  static constexpr int OFF_B0 = SB;      // buffer b at OFF_B0 + b * BUF
+  // Two dS^T buffers (alternating per tile, when LDS allows) let a wave start
+  // the next tile's stream A while others still read this tile's dS^T, so a
+  // tile needs one barrier (after stream A) instead of two.
+  static constexpr int NDS = (2 * SB + NBUF * BUF + 16 <= 160 * 1024 && NBUF == 3) ? 2 : 1;
+  static constexpr int OFF_B0 = NDS * SB;  // buffer b at OFF_B0 + b * BUF
   // K_j, V_j are staged in buffers 1.. at the start of a column (they move to
   // registers before those buffers receive Q tiles)
   static constexpr int OFF_K = OFF_B0 + BUF;
@@ -127,6 +145,8 @@ struct MainCfg {
   // DMA work of one wave for one Q tile, in slots issued one by one between
   // MFMAs: Q and dO rows, the transposed copies (TCOPY), the row terms
   static constexpr int DMA_SLOTS = 2 * DMA_QW + (TCOPY ? 2 * DMA_TW : 0) + 1;
+  // vector-memory instructions of DMA slot u (the row-term slot takes BQ / 64)
+  static constexpr int slot_vmem(int u) { return u < 2 * DMA_QW + (TCOPY ? 2 * DMA_TW : 0) ? 1 : BQ / 64; }
   // Epilogue scratch, aliasing the tile buffers (nothing is in flight then):
   // per output tensor, the fp32 partials of the waves with wq == 1 (NQW == 2)
   // and a padded bf16 tile for coalesced stores.
@@ -193,6 +213,15 @@ struct StreamA {
     const int v = ((k - S0) * U + (E - S0 - 1)) / (E - S0);
     return v < U ? v : U;
   }
+  // vector-memory instructions the DMA slots issue before MFMA k
+  static constexpr int dma_vmem_before(int k) {
+    int n = 0;
+    for (int u = 0; u < dma_before(k); ++u) n += C::slot_vmem(u);
+    return n;
+  }
+  // the previous tile's contribution is published at the top of MFMA kPub
+  static constexpr int kPub = DETATTN_PUB_AT < N ? DETATTN_PUB_AT : N - 1;
+  static_assert(kPub >= 0, "publish slot");
   static constexpr int kUnits = 20;
   static constexpr int kDelay = DETATTN_ELEM_DELAY;
   static constexpr int units_before(int j, int G) {
@@ -308,6 +337,31 @@ __device__ __forceinline__ void lds_barrier() {
 }
 // Wait until at most N vector-memory operations of this wave are in flight
 // (they complete in issue order), then barrier.
+// 16-byte buffer read (per lane: voff + OFF bytes past the resource base plus
+// soff), issued outside the compiler's wait tracking: the caller waits with
+// vm_wait_tied. SC1 selects coherence across XCDs, else within the XCD (sc0).
+template <int OFF, bool SC1>
+__device__ __forceinline__ f32x4 buf_load16_asm(const u32x4& rsrc, uint32_t voff, uint32_t soff) {
+  static_assert(OFF >= 0 && OFF < 4096, "buffer offset field");
+  f32x4 r;
+  if constexpr (SC1)
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen offset:%4 sc1" : "=v"(r) : "v"(voff), "s"(rsrc), "s"(soff), "i"(OFF));
+  else
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen offset:%4 sc0" : "=v"(r) : "v"(voff), "s"(rsrc), "s"(soff), "i"(OFF));
+  return r;
+}
+// wait until at most N vector-memory operations are in flight; x is the
+// register the awaited read filled (it is tied to the wait)
+template <int N>
+__device__ __forceinline__ void vm_wait_tied(f32x4& x) {
+  static_assert(N >= 0 && N <= 63, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%1)" : "+v"(x) : "i"(N));
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N <= 63, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
 template <int N>
 __device__ __forceinline__ void vm_barrier() {
   static_assert(N >= 0 && N <= 63, "vmcnt field");
@@ -665,7 +719,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     trace_rec(6, t_begin, gidx);
 
     int t = t_begin;
-    int b = 0;  // buffer of tile t
+    int* pend = nullptr;  // flag of the previous tile's contribution, not yet published
+    int b = 0;    // buffer of tile t
+    int dsb = 0;  // byte offset of tile t's dS^T buffer
     do {
       const int i = cur.i;
       const int nb = b + 1 == C::NBUF ? 0 : b + 1;  // buffer of tile t+1
@@ -812,7 +868,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
           for (int x = 0; x < 4; ++x) v4[x] = dsB[sq][4 * hh + x];
           const int chunk = (C::QW * wq) / 8 + 2 * sq + hh;
-          *reinterpret_cast<bf16x4*>(smem + oW + ((chunk ^ w_swz) << 4)) = v4;
+          *reinterpret_cast<bf16x4*>(smem + dsb + oW + ((chunk ^ w_swz) << 4)) = v4;
         }
       };
 
@@ -822,6 +878,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       });
       static_for<0, SA::N>([&](auto kc) {
         constexpr int k = decltype(kc)::value;
+        if constexpr (DQM != kDqUnordered && k == SA::kPub) {
+          // publish the previous tile's contribution once its writes have
+          // landed: only this tile's DMA was issued after them, and vector
+          // memory operations complete in issue order
+          if (pend != nullptr) {
+            vm_wait<SA::dma_vmem_before(k)>();
+            if (lane == 0) __hip_atomic_fetch_add(pend, 1, __ATOMIC_RELAXED, kFlagScope);
+            pend = nullptr;
+          }
+        }
         if constexpr (k + PF < SA::N) loadA(std::integral_constant<int, k + PF>{}, ring[(k + PF) % RING]);
         mfmaA(kc, waitA(kc, ring[k % RING]));
         DETATTN_FENCE();
@@ -837,6 +903,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       if constexpr (SA::gsize(C::MQ) == 0)  // one row block: its elementwise work has no MFMAs to hide under
         static_for<0, SA::kUnits>([&](auto uc) { unitA(std::integral_constant<int, C::MQ - 1>{}, uc); });
       trace_rec(1, t, gidx);
+      if constexpr (C::NDS == 2) {
+        // this wave's share of the next tile (DMA issued early in stream A) has
+        // landed: after the barrier below the whole next tile is in LDS
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
 
       // The dQ tile's flag is read now; the load completes under the barrier,
       // and the flag is re-polled after the dQ MFMAs only if the turn has not come.
@@ -858,10 +929,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       using SB_ = StreamB<C>;
       constexpr int NB1 = SB_::NB1;
       constexpr int NB = SB_::N;
-      // MFMA index before which the RMW adds are issued: early when the reads
-      // went out before the dQ MFMAs, later when they wait for the turn
-      constexpr int kAddEarly = NB1 + (SA::NDK * DETATTN_ADD_EARLY) / 8;
+      // atomic modes: MFMA index at which the adds count as issued (trace)
       constexpr int kAddLate = NB1 + (3 * SA::NDK) / 4;
+      // RMW: the NLD 16-byte reads per lane go out under the dQ MFMAs, the
+      // writes under the dV/dK MFMAs, spread so the vector-memory path takes
+      // no burst
+      constexpr int NLD = NQB * 4;
+      constexpr int kStBegin = NB1 + ((NB - NB1) * DETATTN_ST_AT) / 8;
+      auto ld_at = [](int x) constexpr { return (x * ((NB1 * DETATTN_LD_SPAN) / 8)) / NLD; };
+      auto st_at = [](int x) constexpr { return kStBegin + (x * (((NB - NB1) * DETATTN_ST_SPAN) / 8)) / NLD; };
+      static_assert(ld_at(NLD - 1) < NB1 && st_at(NLD - 1) < NB, "RMW slots");
       f32x16 dqAcc[NQB];
 #pragma unroll
       for (int m = 0; m < NQB; ++m) dqAcc[m] = f32x16{};
@@ -876,8 +953,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
         if constexpr (l < SB_::NL1) {
           constexpr int m = l % C::MQD, s = l / C::MQD;
           static_assert(m == 0, "one dS row block per wave");
-          o.lo = lds_tr_asm<16 * s * C::PS>(aS);
-          o.hi = lds_tr_asm<16 * s * C::PS>(aS_hi);
+          o.lo = lds_tr_asm<16 * s * C::PS>(aS + dsb);
+          o.hi = lds_tr_asm<16 * s * C::PS>(aS_hi + dsb);
         } else {
           constexpr int x = l - SB_::NL1, kind = 2 + (x & 1), st = x >> 1;
           constexpr int sq = 2 * (C::MQ - 1) + st / C::ND, n = st % C::ND;
@@ -909,8 +986,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       };
       // register group h of block mb: one 16-byte access per lane, cache scope of the mode
       constexpr int kAux = kScope == __HIP_MEMORY_SCOPE_WORKGROUP ? kBufSc0 : kBufSc1;
-      auto dq_load4 = [&](int mb, int h) -> f32x4 {
-        return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(dqrsrc, dqlane[mb] + h * 1024, dqtile, kAux));
+      // reads: the first contributor reads a zero-length view (every read out
+      // of range returns 0); the resource words are uniform (SGPRs)
+      u32x4 ldrsrc;
+      {
+        const uint64_t p = reinterpret_cast<uint64_t>(a.dqacc + head_off);
+        ldrsrc[0] = __builtin_amdgcn_readfirstlane((uint32_t)p);
+        ldrsrc[1] = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xFFFFu);
+        ldrsrc[2] = __builtin_amdgcn_readfirstlane(rk > 0 ? (uint32_t)(a.S * D * 4) : 0u);
+        ldrsrc[3] = (uint32_t)kBufferWord3;
+      }
+      auto dq_load4 = [&](auto xc) -> f32x4 {
+        constexpr int x = decltype(xc)::value;
+        return buf_load16_asm<(x % 4) * 1024, kAux == kBufSc1>(ldrsrc, dqlane[x / 4], (uint32_t)dqtile);
       };
       auto dq_store4 = [&](int mb, int h, f32x4 v) {
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), dqrsrc, dqlane[mb] + h * 1024, dqtile, kAux);
@@ -943,20 +1031,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
       };
-      // RMW modes: read the accumulator (after the turn has come)
+      // RMW modes: read the whole accumulator again (after a late turn) and wait for it
       auto rmw_loads = [&]() {
-        if (rk > 0) {
-          if constexpr (DQM == kDqLocalRmw) asm volatile("buffer_inv sc0" ::: "memory");
-#pragma unroll
-          for (int m = 0; m < NQB; ++m)
-#pragma unroll
-            for (int h = 0; h < 4; ++h) old[m][h] = dq_load4(m, h);
-        } else {
-#pragma unroll
-          for (int m = 0; m < NQB; ++m)
-#pragma unroll
-            for (int h = 0; h < 4; ++h) old[m][h] = f32x4{};
-        }
+        if constexpr (DQM == kDqLocalRmw) asm volatile("buffer_inv sc0" ::: "memory");
+        static_for<0, NLD>([&](auto xc) {
+          constexpr int x = decltype(xc)::value;
+          old[x / 4][x % 4] = dq_load4(xc);
+        });
+        static_for<0, NLD>([&](auto xc) {
+          constexpr int x = decltype(xc)::value;
+          vm_wait_tied<0>(old[x / 4][x % 4]);
+        });
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
       };
       // after the dQ MFMAs: wait for the turn if it had not come (RMW: then read
@@ -993,38 +1078,55 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
           __atomic_signal_fence(__ATOMIC_SEQ_CST);
         }
       };
-      auto adds_finish = [&]() {
-        if constexpr (kRmw) {
-#pragma unroll
-          for (int m = 0; m < NQB; ++m)
-#pragma unroll
-            for (int h = 0; h < 4; ++h) dq_store4(m, h, old[m][h] + acc4(m, h));
-          __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        }
-        trace_rec(4, t, gidx);
-      };
+      auto adds_finish = [&]() { trace_rec(4, t, gidx); };
 
       if constexpr (kRmw) {
+        // early: the turn has come, the accumulator is read under the first dQ
+        // MFMAs (local mode drops stale L1 lines first); otherwise it is read
+        // after waiting for the turn
         if (early) {
+          if constexpr (DQM == kDqLocalRmw) asm volatile("buffer_inv sc0" ::: "memory");
           trace_rec(3, t, gidx);
-          rmw_loads();
         }
       }
       static_for<0, PF>([&](auto lc) { loadB(lc, ring[decltype(lc)::value]); });
       static_for<0, NB>([&](auto kc) {
         constexpr int k = decltype(kc)::value;
+        if constexpr (kRmw) {
+          static_for<0, NLD>([&](auto xc) {
+            constexpr int x = decltype(xc)::value;
+            // only once the turn has been seen: the accumulator is never read
+            // (nor cached) before the previous contributor's adds are visible
+            if constexpr (ld_at(x) == k) {
+              if (early) old[x / 4][x % 4] = dq_load4(xc);
+            }
+          });
+        }
         if constexpr (k == NB1) {
           DETATTN_FENCE();
           trace_rec(2, t, gidx);
           adds_begin();
           DETATTN_FENCE();
         }
-        if constexpr (kRmw && k == kAddEarly) {
-          if (early) adds_finish();
-          DETATTN_FENCE();
+        if constexpr (kRmw) {
+          static_for<0, NLD>([&](auto xc) {
+            constexpr int x = decltype(xc)::value;
+            if constexpr (st_at(x) == k) {
+              if constexpr (x == 0) {
+                // every read has landed (only reads are in flight before the
+                // first write, so one full wait covers them all)
+                static_for<0, NLD>([&](auto yc) {
+                  constexpr int y = decltype(yc)::value;
+                  vm_wait_tied<0>(old[y / 4][y % 4]);
+                });
+              }
+              dq_store4(x / 4, x % 4, old[x / 4][x % 4] + acc4(x / 4, x % 4));
+              if constexpr (x == NLD - 1) adds_finish();
+            }
+          });
         }
-        if constexpr (k == kAddLate) {
-          if (!kRmw || !early) adds_finish();
+        if constexpr (!kRmw && k == kAddLate) {
+          adds_finish();
           DETATTN_FENCE();
         }
         // loads that may be issued now (pf loads ahead of this MFMA's own)
@@ -1043,25 +1145,29 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       });
 
       trace_rec(5, t, gidx);
-      // This wave's adds (and the next tile's DMA, issued earlier) are
-      // complete: publish the wave's share of the contribution right away.
+      // The wave publishes its share of the contribution once its adds have
+      // landed: early in the next tile's stream A, or at the end of the column.
       // The flag counts wave contributions, so no barrier sits between the
       // adds and the hand-off to the next contributor.
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       if constexpr (DQM != kDqUnordered) {
         const bool withhold = (a.skip_item >= 0 && gidx == a.skip_item && t == 0);
-        if (lane == 0 && !withhold) __hip_atomic_fetch_add(flag, 1, __ATOMIC_RELAXED, kFlagScope);
+        pend = withhold ? nullptr : flag;
       }
       ++t;
       if (t >= t_end) break;
       cur = nxt;
       b = nb;
-      lds_barrier();  // the next tile's data is in LDS in every wave's share
+      if constexpr (C::NDS == 2) dsb ^= C::SB;
+      else lds_barrier();  // the next tile's data is in LDS in every wave's share
     } while (true);  // tiles of the segment
 
     // ---- end of a column: dK, dV of KV tile j to global ----
     mfma_agpr_drain();
     wait_vm_all();
+    if (pend != nullptr) {
+      if (lane == 0) __hip_atomic_fetch_add(pend, 1, __ATOMIC_RELAXED, kFlagScope);
+      pend = nullptr;
+    }
     __syncthreads();
     {
       float* red = reinterpret_cast<float*>(smem);
