@@ -57,6 +57,10 @@
 //   DMA_SPAN   the next tile's DMA is spread over this fraction (1/8ths) of stream A
 //   PUB_AT     stream-A MFMA of the next tile before which a wave publishes its
 //              previous tile's dQ contribution
+//   FLAG_AT    stream-A MFMA (in 1/8ths of stream A) before which the dQ tile's
+//              flag is read, so its latency hides under the rest of stream A
+//   DECIDE_AT  stream-B MFMA before which the flag value is examined (its
+//              latency hides under the first dQ MFMAs) and the reads begin
 //   LD_SPAN    the dQ accumulator reads are spread over this fraction (1/8ths)
 //              of the dQ MFMAs (0: all before the first)
 //   ST_AT, ST_SPAN  the accumulator writes start after this fraction (1/8ths)
@@ -72,6 +76,12 @@
 #endif
 #ifndef DETATTN_PUB_AT
 #define DETATTN_PUB_AT 4
+#endif
+#ifndef DETATTN_FLAG_AT
+#define DETATTN_FLAG_AT 7
+#endif
+#ifndef DETATTN_DECIDE_AT
+#define DETATTN_DECIDE_AT 2
 #endif
 #ifndef DETATTN_LD_SPAN
 #define DETATTN_LD_SPAN 0
@@ -221,6 +231,9 @@ struct StreamA {
   }
   // the previous tile's contribution is published at the top of MFMA kPub
   static constexpr int kPub = DETATTN_PUB_AT < N ? DETATTN_PUB_AT : N - 1;
+  static constexpr int kFlag = (N * DETATTN_FLAG_AT) / 8 < N ? (N * DETATTN_FLAG_AT) / 8 : N - 1;
+  // the flag read is the last vector-memory operation of stream A
+  static_assert(dma_before(kFlag) == C::DMA_SLOTS, "every DMA slot precedes the flag read");
   static_assert(kPub >= 0, "publish slot");
   static constexpr int kUnits = 20;
   static constexpr int kDelay = DETATTN_ELEM_DELAY;
@@ -326,6 +339,20 @@ struct Opnd {
   u32x2 lo, hi;
 };
 __device__ __forceinline__ u32x4 cat2(const u32x2& a, const u32x2& b) { return u32x4{a[0], a[1], b[0], b[1]}; }
+// one wait for two operands (Q0/Q1: the operand is a 16-byte read, else two
+// transposing halves); every register of both is tied to the wait
+template <int N, bool Q0, bool Q1>
+__device__ __forceinline__ void lgkm_wait2(Opnd& a, Opnd& b) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt field");
+  if constexpr (Q0 && Q1)
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a.q), "+v"(b.q) : "i"(N));
+  else if constexpr (Q0)
+    asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(a.q), "+v"(b.lo), "+v"(b.hi) : "i"(N));
+  else if constexpr (Q1)
+    asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(a.lo), "+v"(a.hi), "+v"(b.q) : "i"(N));
+  else
+    asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a.lo), "+v"(a.hi), "+v"(b.lo), "+v"(b.hi) : "i"(N));
+}
 
 // Workgroup barrier for LDS hand-offs only: LDS operations are complete, but
 // vector-memory loads in flight (the prefetch DMA) stay in flight.
@@ -528,6 +555,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   int dqlane[NQB];
 #pragma unroll
   for (int mb = 0; mb < NQB; ++mb) dqlane[mb] = dqblk(mb) + lane * 16;
+  // The atomic modes keep the accumulator row-major instead (their per-element
+  // atomics then touch two 128-byte lines per instruction, not eight): lane
+  // offset of row 32 mq0 + 4g, column 32 nbq + lane%32
+  const int dqlane_rm = ((32 * mq0 + 4 * g) * D + 32 * nbq + c32) * 4;
   int goffQ[C::DMA_QW];
 #pragma unroll
   for (int x = 0; x < C::DMA_QW; ++x) goffQ[x] = dma_goff<C::NCH>(w + 4 * x, lane);
@@ -765,6 +796,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       // this tile's turn in dQ tile i's order: rank rk; the flag counts the wave contributions added
       const int rk = DQM == kDqUnordered ? 0 : cur.rank_now();
       int* flag = a.flags + ((long long)bh * sc.n_q + i) * kFlagInts;
+      int seen = rk;  // the flag as last read (read in stream A)
       const int vb = C::OFF_B0 + b * C::BUF;
       const int vL = oL + vb;
       const uint32_t aA = lbase + oA + vb, aT = lbase + oT + vb, aQT = lbase + oQT + vb;
@@ -888,8 +920,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
             pend = nullptr;
           }
         }
+        if constexpr (DQM != kDqUnordered && k == SA::kFlag) {
+          // the dQ tile's flag, read late in stream A (every lane reads the
+          // same word; also by the first contributor, so this read is always
+          // the wave's newest vector-memory operation at the barrier); it is
+          // re-polled after the dQ MFMAs only if the turn had not come
+          seen = __hip_atomic_load(flag, __ATOMIC_RELAXED, kFlagScope);
+        }
         if constexpr (k + PF < SA::N) loadA(std::integral_constant<int, k + PF>{}, ring[(k + PF) % RING]);
-        mfmaA(kc, waitA(kc, ring[k % RING]));
+        // operands are awaited in pairs: the even MFMA's wait also covers the
+        // next one, which then needs neither a wait nor a hazard gap
+        constexpr bool q0 = SA::sdp(k) || C::TCOPY;
+        if constexpr (k % 2 == 0 && k + 1 < SA::N) {
+          constexpr bool q1 = SA::sdp(k + 1) || C::TCOPY;
+          lgkm_wait2<SA::loads_after(k + 1, PF - 1), q0, q1>(ring[k % RING], ring[(k + 1) % RING]);
+          mfmaA(kc, q0 ? ring[k % RING].q : cat2(ring[k % RING].lo, ring[k % RING].hi));
+        } else if constexpr (k % 2 == 1) {
+          mfmaA(kc, q0 ? ring[k % RING].q : cat2(ring[k % RING].lo, ring[k % RING].hi));
+        } else {
+          mfmaA(kc, waitA(kc, ring[k % RING]));
+        }
         DETATTN_FENCE();
         static_for<SA::dma_before(k), SA::dma_before(k + 1)>([&](auto uc) { dma_slot(uc); });
         constexpr int gi = SA::group(k);
@@ -903,27 +953,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       if constexpr (SA::gsize(C::MQ) == 0)  // one row block: its elementwise work has no MFMAs to hide under
         static_for<0, SA::kUnits>([&](auto uc) { unitA(std::integral_constant<int, C::MQ - 1>{}, uc); });
       trace_rec(1, t, gidx);
-      if constexpr (C::NDS == 2) {
-        // this wave's share of the next tile (DMA issued early in stream A) has
-        // landed: after the barrier below the whole next tile is in LDS
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
+      // this wave's share of the next tile (DMA issued early in stream A) has
+      // landed: after the barrier below the whole next tile is in LDS. The
+      // flag read, issued after it, may stay in flight.
+      vm_wait<DQM != kDqUnordered ? 1 : 0>();
 
-      // The dQ tile's flag is read now; the load completes under the barrier,
-      // and the flag is re-polled after the dQ MFMAs only if the turn has not come.
-      int seen = rk;
-      if (DQM != kDqUnordered && rk > 0 && lane == 0) seen = __hip_atomic_load(flag, __ATOMIC_RELAXED, kFlagScope);
       // The turn has come once every wave of every earlier contributor has
       // added: flag >= kWaves * rk. The counter only grows, and a wave of this
       // workgroup adds only after seeing the turn, so a larger value (a
       // sibling wave already done) also means the turn has come.
       const int turn_val = kWaves * rk;
       lds_barrier();  // dS^T complete
-      // early: the turn has come already (or this is the first contribution),
-      // so the accumulator is read right away and the adds are issued early;
-      // the delay injection of the tests always takes the late path
-      const bool early = DQM != kDqUnordered &&
-                         (rk == 0 || (a.delay_seed == 0 && __builtin_amdgcn_readfirstlane(seen) >= turn_val));
+      // early (decided at stream-B MFMA kDecide): the turn has come already (or
+      // this is the first contribution), so the accumulator is read right away
+      // and the adds are issued early; the delay injection of the tests always
+      // takes the late path
+      bool early = false;
 
       // ---- stream B: dQ partial = dS K (this wave's DW column blocks x MQD row blocks), then dV/dK of the last block ----
       using SB_ = StreamB<C>;
@@ -935,8 +980,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       // writes under the dV/dK MFMAs, spread so the vector-memory path takes
       // no burst
       constexpr int NLD = NQB * 4;
+      constexpr int kDecide = DETATTN_DECIDE_AT < NB1 ? DETATTN_DECIDE_AT : 0;
       constexpr int kStBegin = NB1 + ((NB - NB1) * DETATTN_ST_AT) / 8;
-      auto ld_at = [](int x) constexpr { return (x * ((NB1 * DETATTN_LD_SPAN) / 8)) / NLD; };
+      auto ld_at = [](int x) constexpr { return kDecide + (x * (((NB1 - kDecide) * DETATTN_LD_SPAN) / 8)) / NLD; };
       auto st_at = [](int x) constexpr { return kStBegin + (x * (((NB - NB1) * DETATTN_ST_SPAN) / 8)) / NLD; };
       static_assert(ld_at(NLD - 1) < NB1 && st_at(NLD - 1) < NB, "RMW slots");
       f32x16 dqAcc[NQB];
@@ -980,9 +1026,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
           else mfma_agpr(dKacc[n], dsB[sq], opr);
         }
       };
-      // element r of block mb (atomic modes): (uniform tile base) + (32-bit lane offset)
+      // element r of block mb, row-major (atomic modes): (uniform tile base) + (32-bit lane offset)
       auto dqp = [&](int mb, int r) -> float* {
-        return reinterpret_cast<float*>(dqbase + (uint32_t)(dqlane[mb] + (r >> 2) * 1024 + (r & 3) * 4));
+        const int m = mb / C::DW, n = mb % C::DW;
+        return reinterpret_cast<float*>(dqbase +
+                                        (uint32_t)(dqlane_rm + (32 * m + 8 * (r >> 2) + (r & 3)) * D * 4 + 32 * n * 4));
       };
       // register group h of block mb: one 16-byte access per lane, cache scope of the mode
       constexpr int kAux = kScope == __HIP_MEMORY_SCOPE_WORKGROUP ? kBufSc0 : kBufSc1;
@@ -1065,7 +1113,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
               for (int m = 0; m < NQB; ++m)
 #pragma unroll
-                for (int h = 0; h < 4; ++h) dq_store4(m, h, acc4(m, h));
+                for (int r = 0; r < 16; ++r)
+                  __hip_atomic_store(dqp(m, r), dqAcc[m][r], __ATOMIC_RELAXED, kScope);
             } else {
 #pragma unroll
               for (int m = 0; m < NQB; ++m)
@@ -1080,18 +1129,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       };
       auto adds_finish = [&]() { trace_rec(4, t, gidx); };
 
-      if constexpr (kRmw) {
-        // early: the turn has come, the accumulator is read under the first dQ
-        // MFMAs (local mode drops stale L1 lines first); otherwise it is read
-        // after waiting for the turn
-        if (early) {
-          if constexpr (DQM == kDqLocalRmw) asm volatile("buffer_inv sc0" ::: "memory");
-          trace_rec(3, t, gidx);
-        }
-      }
       static_for<0, PF>([&](auto lc) { loadB(lc, ring[decltype(lc)::value]); });
       static_for<0, NB>([&](auto kc) {
         constexpr int k = decltype(kc)::value;
+        if constexpr (k == kDecide && DQM != kDqUnordered) {
+          early = rk == 0 || (a.delay_seed == 0 && __builtin_amdgcn_readfirstlane(seen) >= turn_val);
+          // early: the turn has come, the accumulator is read under the dQ MFMAs
+          // (local mode drops stale L1 lines first); otherwise it is read after
+          // waiting for the turn
+          if (early) {
+            if constexpr (DQM == kDqLocalRmw) asm volatile("buffer_inv sc0" ::: "memory");
+            trace_rec(3, t, gidx);
+          }
+        }
         if constexpr (kRmw) {
           static_for<0, NLD>([&](auto xc) {
             constexpr int x = decltype(xc)::value;
@@ -1134,13 +1184,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
         static_for<l0, l1 + 1>([&](auto lc) { loadB(lc, ring[decltype(lc)::value % RING]); });
         constexpr int l = SB_::load_of(k);
         Opnd& o = ring[l % RING];
-        if constexpr (k >= NB1 && C::TCOPY) {
-          lgkm_wait<SB_::insts_after(k, PF)>(o.q);
-          mfmaB(kc, o.q);
-        } else {
-          if constexpr (SB_::first_use(k)) lgkm_wait<SB_::insts_after(k, PF)>(o.lo, o.hi);
-          mfmaB(kc, cat2(o.lo, o.hi));
+        // operands are awaited in pairs of loads (l even: l and l + 1)
+        constexpr bool qo = k >= NB1 && C::TCOPY;
+        if constexpr (SB_::first_use(k) && l % 2 == 0) {
+          if constexpr (l + 1 < SB_::NL) {
+            constexpr bool q1 = l + 1 >= SB_::NL1 && C::TCOPY;
+            lgkm_wait2<SB_::insts_after(k, PF) - SB_::ninst(l + 1), qo, q1>(o, ring[(l + 1) % RING]);
+          } else if constexpr (qo) {
+            lgkm_wait<SB_::insts_after(k, PF)>(o.q);
+          } else {
+            lgkm_wait<SB_::insts_after(k, PF)>(o.lo, o.hi);
+          }
         }
+        if constexpr (qo) mfmaB(kc, o.q);
+        else mfmaB(kc, cat2(o.lo, o.hi));
         DETATTN_FENCE();
       });
 

@@ -291,7 +291,8 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
     (void)hipGetLastError();
     return e == hipErrorCooperativeLaunchTooLarge ? DETATTN_ERR_UNSUPPORTED : DETATTN_ERR_HIP;
   }
-  e = launch_convert(s.D, dqacc, static_cast<__bf16*>(dq), rows, s.softmax_scale, st_);
+  const bool fragment_order = P.dqm_internal == kDqOrderedRmw || P.dqm_internal == kDqLocalRmw;
+  e = launch_convert(s.D, dqacc, static_cast<__bf16*>(dq), rows, s.softmax_scale, fragment_order, st_);
   return e == hipSuccess ? DETATTN_OK : DETATTN_ERR_HIP;
 }
 

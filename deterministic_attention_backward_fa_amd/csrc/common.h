@@ -45,7 +45,8 @@ static constexpr int kBufferWord3 = 0x00020000;
 static constexpr int kBufSc0 = 1;
 static constexpr int kBufSc1 = 16;
 
-// The fp32 dQ accumulator is kept in MFMA fragment order: rows in 32-row
+// The fp32 dQ accumulator of the read-modify-write modes is kept in MFMA
+// fragment order (the atomic modes keep it row-major): rows in 32-row
 // blocks, each block as D/32 column blocks of 32 x 32; inside such a block the
 // element (row 8h + 4g + e, column c) sits at float (h * 64 + 32g + c) * 4 + e,
 // so one lane's four accumulator registers 4h .. 4h+3 are 16 contiguous bytes.

@@ -5,7 +5,24 @@
 
 namespace detattn {
 
-// dQ = bf16_rne(scale * acc). The accumulator is in fragment order
+// dQ = bf16_rne(scale * acc) from a row-major accumulator, 8 elements per thread.
+__global__ __launch_bounds__(256) void bwd_convert_rm_kernel(const float* __restrict__ acc, __bf16* __restrict__ dq,
+                                                             long long n8, float scale) {
+  const long long gsz = (long long)gridDim.x * 256;
+  for (long long x = (long long)blockIdx.x * 256 + threadIdx.x; x < n8; x += gsz) {
+    const f32x4 a = reinterpret_cast<const f32x4*>(acc)[2 * x];
+    const f32x4 b = reinterpret_cast<const f32x4*>(acc)[2 * x + 1];
+    bf16x8 r;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      r[t] = (__bf16)(scale * a[t]);
+      r[4 + t] = (__bf16)(scale * b[t]);
+    }
+    reinterpret_cast<bf16x8*>(dq)[x] = r;
+  }
+}
+
+// dQ = bf16_rne(scale * acc) from an accumulator in fragment order
 // (dqacc_index): a workgroup takes 32-row blocks, reads each block's 16-byte
 // runs, and writes the rows through LDS as 16-byte runs.
 template <int D>
@@ -67,7 +84,14 @@ hipError_t launch_transpose(int D, const __bf16* q, const __bf16* dout, __bf16* 
   return hipGetLastError();
 }
 
-hipError_t launch_convert(int D, const float* acc, __bf16* dq, long long rows, float scale, hipStream_t st) {
+hipError_t launch_convert(int D, const float* acc, __bf16* dq, long long rows, float scale, bool fragment_order,
+                          hipStream_t st) {
+  if (!fragment_order) {
+    const long long n8 = rows * D / 8;
+    const int g = grid_for(n8, 256, 256 * 16);
+    bwd_convert_rm_kernel<<<dim3(g), dim3(256), 0, st>>>(acc, dq, n8, scale);
+    return hipGetLastError();
+  }
   const long long rb = rows / 32;
   const int g = grid_for(rb, 1, 256 * 16);
   if (D == 64)

@@ -43,7 +43,10 @@ hipError_t launch_pre(int D, const __bf16* o, const __bf16* dout, const float* l
                       long long n_flags, unsigned* header, float* dqacc, long long dqacc_elems, hipStream_t st);
 hipError_t launch_transpose(int D, const __bf16* q, const __bf16* dout, __bf16* qt, __bf16* dot, long long BH, int S,
                             hipStream_t st);
-hipError_t launch_convert(int D, const float* acc, __bf16* dq, long long rows, float scale, hipStream_t st);
+// fragment_order: the accumulator layout of the read-modify-write dQ modes
+// (dqacc_index); otherwise row-major (atomic modes)
+hipError_t launch_convert(int D, const float* acc, __bf16* dq, long long rows, float scale, bool fragment_order,
+                          hipStream_t st);
 hipError_t launch_main(const MainLaunch& L, hipStream_t st);
 hipError_t launch_fwd(int D, int causal, const __bf16* q, const __bf16* k, const __bf16* v, __bf16* o, float* lse,
                       int BH, int S, float scale, hipStream_t st);
