@@ -13,7 +13,6 @@ MainInfo info_of() {
     auto fn = &bwd_main_kernel<D, BQ, BKV, CAUSAL, DQM, TRACE>;
     m.func = reinterpret_cast<const void*>(fn);
     m.lds_bytes = MainCfg<D, BQ, BKV>::LDS_BYTES;
-    m.tcopy = MainCfg<D, BQ, BKV>::TCOPY ? 1 : 0;
     int occ = 0;
     if (hipFuncSetAttribute(m.func, hipFuncAttributeMaxDynamicSharedMemorySize, m.lds_bytes) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kThreads, m.lds_bytes) != hipSuccess)
@@ -32,7 +31,7 @@ MainInfo pick_mode(int dqm) {
     case kDqOrderedAtomic: return info_of<D, BQ, BKV, CAUSAL, kDqOrderedAtomic, TRACE>();
     case kDqUnordered: return info_of<D, BQ, BKV, CAUSAL, kDqUnordered, TRACE>();
     case kDqLocalRmw: return info_of<D, BQ, BKV, CAUSAL, kDqLocalRmw, TRACE>();
-    default: return MainInfo{nullptr, 0, 0, 0};
+    default: return MainInfo{nullptr, 0, 0};
   }
 }
 

@@ -32,8 +32,6 @@ struct BwdArgs {
   const __bf16* k;
   const __bf16* v;
   const __bf16* dout;
-  const __bf16* qt;    // Q per head as [D][S], 16-row groups in accumulator K order (bwd_transpose_kernel)
-  const __bf16* dot;   // dO, same layout
   const float* nlse;   // -LSE / scale per row (initial value of the S accumulator)
   const float* ndelta; // -D per row (initial value of the dP accumulator)
   float* dqacc;
@@ -110,44 +108,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Q and dO per head transposed to [D][S] for the main kernel's dV, dK
-// operands, which then load with 16-byte LDS reads. Inside every 16
-// consecutive rows the order is 0-3, 8-11, 4-7, 12-15: the K order of an MFMA
-// operand taken from an accumulator tile (lane group g holds rows 4g..4g+3
-// and 8+4g..8+4g+3), so position p holds row p with bits 2 and 3 swapped.
-// One workgroup per 64 rows of one head; the tile goes through LDS so both
-// the reads and the writes are coalesced.
-// ---------------------------------------------------------------------------
-__host__ __device__ constexpr int qt_perm16(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
-
-template <int D>
-__global__ __launch_bounds__(256) void bwd_transpose_kernel(const __bf16* __restrict__ q,
-                                                            const __bf16* __restrict__ dout, __bf16* __restrict__ qt,
-                                                            __bf16* __restrict__ dot, int S) {
-  constexpr int P = D + 8;  // padded LDS row (elements)
-  __shared__ __attribute__((aligned(16))) __bf16 tile[64 * P];
-  const long long bh = blockIdx.y;
-  const int q0 = blockIdx.x * 64;
-  const int tid = threadIdx.x;
-#pragma unroll 1
-  for (int ten = 0; ten < 2; ++ten) {
-    const __bf16* src = (ten == 0 ? q : dout) + (bh * S + q0) * D;
-    __bf16* dst = (ten == 0 ? qt : dot) + bh * S * D + q0;
-    for (int c = tid; c < 64 * D / 8; c += 256) {
-      const int r = c / (D / 8), x = c % (D / 8);
-      *reinterpret_cast<bf16x8*>(tile + r * P + 8 * x) = *reinterpret_cast<const bf16x8*>(src + r * D + 8 * x);
-    }
-    __syncthreads();
-    for (int c = tid; c < D * 8; c += 256) {
-      const int d = c / 8, p8 = c % 8;
-      bf16x8 v;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = tile[qt_perm16(8 * p8 + e) * P + d];
-      *reinterpret_cast<bf16x8*>(dst + (long long)d * S + 8 * p8) = v;
-    }
-    __syncthreads();
-  }
-}
 
 }  // namespace detattn
 

@@ -23,27 +23,35 @@
 // accumulator at -D_q (so dS = P * acc). Causal masking sets the S initial
 // value to -inf above the diagonal, on diagonal tiles only.
 //
-// Instruction stream of one tile (one wave runs per SIMD, so MFMA, VALU and
-// LDS work overlap only when interleaved in the wave's own stream):
-//   top:   wait for this tile's LDS-DMA data and the previous tile's dQ adds,
-//          barrier, publish the previous tile's flag, DMA tile t+1 into the
-//          other buffer;
-//   A:     MFMA stream S/dP of row block 0, S/dP of block 1 (+ elementwise of
-//          block 0 between its MFMAs), dV/dK of block 0 (+ elementwise of
-//          block 1), ..., with the dS^T stores to LDS among the elementwise
-//          work; every MFMA's LDS operand is loaded PF MFMAs ahead;
-//   barrier (dS^T complete);
-//   B:     dQ partial MFMAs; wait for the dQ tile's turn; read the
-//          accumulator; dV/dK MFMAs of the last row block, with the
-//          accumulator adds placed among them.
-// The accumulator is touched only through coherent accesses (agent scope, or
-// workgroup scope when a ring of workgroups shares one XCD's L2), so the
-// hand-off needs no cache writeback: "all adds done" is vmcnt 0 in every wave
-// before the barrier that precedes the flag store.
+// Instruction streams of one tile (one wave runs per SIMD, so MFMA, VALU,
+// LDS and memory work overlap only when interleaved in the wave's own stream):
+//   top:   row terms of tile t as the accumulators' initial values (the
+//          diagonal mask on diagonal tiles);
+//   A:     S/dP MFMAs of row block 0, S/dP of block 1 with block 0's
+//          elementwise work (exp2, dS, bf16 packing, dS^T stores) between
+//          them, dV/dK of block 0 with block 1's elementwise work. Every MFMA's
+//          LDS operand is read PF MFMAs ahead; the previous tile's dQ
+//          contribution is published (flag += 1 per wave) once its writes have
+//          landed; tile t+1's Q, dO and row terms are DMA'd (global_load_lds)
+//          into the next of three buffers over the first half; the dQ tile's
+//          flag is read near the end;
+//   barrier (dS^T complete, tile t+1 in LDS): the one barrier of the tile;
+//   B:     dQ partial MFMAs (dS^T from LDS, K^T from registers); if the turn
+//          has come (flag >= 4 * rank), the accumulator is read under them,
+//          else after a bounded wait; dV/dK MFMAs of the last row block, with
+//          the accumulator writes spread among the first of them.
+// dS^T alternates between two LDS buffers, so a wave may start stream A of
+// tile t+1 while others still read tile t's dS^T. The accumulator is touched
+// only through coherent accesses (agent scope, or workgroup scope plus an L1
+// invalidate when a ring of workgroups shares one XCD's L2), so the hand-off
+// needs no cache writeback: a wave's writes have landed once its vmcnt
+// covers them, before it adds to the flag.
 //
-// LDS tiles are row-major with 16 bytes of padding per row: 16 consecutive
-// rows read at one column start on 16 different 4-bank groups, and every
-// fragment address is one per-lane register plus a compile-time offset.
+// LDS tiles of Q, dO, K, V are row-major with 16 bytes of padding per row and
+// rows permuted inside 16-row blocks (rperm), which keeps both the row and the
+// transposing fragment reads free of bank conflicts; dS^T is unpadded with an
+// XOR swizzle of its 16-byte chunks. Every fragment address is one per-lane
+// register plus a compile-time offset.
 #pragma once
 #include "common.h"
 #include "tile_sched.h"
@@ -119,27 +127,17 @@ struct MainCfg {
   static constexpr int KB = BKV * PD;    // one K or V tile
   static constexpr int SB = BKV * PS;    // dS^T tile (row kv, column q)
   static constexpr int LDB = BQ * 8;     // -LSE/scale then -D, fp32
-  // Transposed copies of Q and dO ([D][BQ] per tile, padded rows) feed the dV,
-  // dK products with 16-byte reads; without them those operands are read
-  // from the row tiles with transposing reads (used where LDS is too small).
-  static constexpr int PT = BQ * 2 + 16;
-  static constexpr int QTB = D * PT;
-  // Measured on MI355X: the extra DMA traffic of the copies costs more than
-  // the transposing reads they replace, so they are off.
-  static constexpr bool kUseTransposedCopies = false;
-  static constexpr bool TCOPY = kUseTransposedCopies && SB + 2 * (2 * QB + 2 * QTB + LDB) + 16 <= 160 * 1024;
-  static constexpr int OFF_QT = 2 * QB;  // inside a buffer (TCOPY)
-  static constexpr int OFF_LD = 2 * QB + (TCOPY ? 2 * QTB : 0);
-  static constexpr int BUF = OFF_LD + LDB;  // one Q-tile buffer: Q, dO, [Q^T, dO^T], row terms
+  static constexpr int OFF_LD = 2 * QB;
+  static constexpr int BUF = OFF_LD + LDB;  // one Q-tile buffer: Q, dO, row terms
   static constexpr int OFF_DS = 0;
-  // Q-tile buffers: the next tile is loaded one tile ahead; a third buffer
-  // (when LDS allows) gives K_j, V_j room to be staged at the start of a
-  // column next to the first Q tile
-  static constexpr int NBUF = TCOPY ? 2 : 3;
+  // Q-tile buffers: the next tile is loaded one tile ahead; the third buffer
+  // gives K_j, V_j room to be staged at the start of a column next to the
+  // first Q tile, and lets one barrier per tile suffice
+  static constexpr int NBUF = 3;
   // Two dS^T buffers (alternating per tile, when LDS allows) let a wave start
   // the next tile's stream A while others still read this tile's dS^T, so a
   // tile needs one barrier (after stream A) instead of two.
-  static constexpr int NDS = (2 * SB + NBUF * BUF + 16 <= 160 * 1024 && NBUF == 3) ? 2 : 1;
+  static constexpr int NDS = (2 * SB + NBUF * BUF + 16 <= 160 * 1024) ? 2 : 1;
   static constexpr int OFF_B0 = NDS * SB;  // buffer b at OFF_B0 + b * BUF
   // K_j, V_j are staged in buffers 1.. at the start of a column (they move to
   // registers before those buffers receive Q tiles)
@@ -149,14 +147,11 @@ struct MainCfg {
   static constexpr int DMA_Q = BQ * (NCH + 1) / 64;  // 1 KB DMA instructions per padded Q/dO tile
   static constexpr int DMA_K = BKV * (NCH + 1) / 64;
   static constexpr int DMA_QW = (DMA_Q + 3) / 4;     // per wave, at most
-  static constexpr int NCT = BQ / 8;                 // 16-byte chunks per transposed row
-  static constexpr int DMA_T = D * (NCT + 1) / 64;   // per padded transposed tile
-  static constexpr int DMA_TW = (DMA_T + 3) / 4;
   // DMA work of one wave for one Q tile, in slots issued one by one between
-  // MFMAs: Q and dO rows, the transposed copies (TCOPY), the row terms
-  static constexpr int DMA_SLOTS = 2 * DMA_QW + (TCOPY ? 2 * DMA_TW : 0) + 1;
+  // MFMAs: Q and dO rows, then the row terms
+  static constexpr int DMA_SLOTS = 2 * DMA_QW + 1;
   // vector-memory instructions of DMA slot u (the row-term slot takes BQ / 64)
-  static constexpr int slot_vmem(int u) { return u < 2 * DMA_QW + (TCOPY ? 2 * DMA_TW : 0) ? 1 : BQ / 64; }
+  static constexpr int slot_vmem(int u) { return u < 2 * DMA_QW ? 1 : BQ / 64; }
   // Epilogue scratch, aliasing the tile buffers (nothing is in flight then):
   // per output tensor, the fp32 partials of the waves with wq == 1 (NQW == 2)
   // and a padded bf16 tile for coalesced stores.
@@ -172,7 +167,6 @@ struct MainCfg {
   static_assert((BQ * (NCH + 1)) % 64 == 0 && (BKV * (NCH + 1)) % 64 == 0, "DMA granularity");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(OFF_V + KB <= TILE_END, "K, V staging");
-  static_assert(!TCOPY || (D * (NCT + 1)) % 64 == 0, "DMA granularity");
 };
 
 // Order of the MFMAs of stream A (before the dS^T barrier). Group gi holds the
@@ -204,7 +198,7 @@ struct StreamA {
   static constexpr int step(int k) { return sdp(k) ? (rel(k) >> 1) : (drel(k) >> 1); }
   // LDS instructions of MFMA k's operand load, and those issued after it by
   // the time MFMA k runs (operands are loaded pf MFMAs ahead)
-  static constexpr int nloads(int k) { return (sdp(k) || C::TCOPY) ? 1 : 2; }
+  static constexpr int nloads(int k) { return sdp(k) ? 1 : 2; }
   static constexpr int loads_after(int k, int pf) {
     int n = 0;
     for (int x = k + 1; x <= k + pf && x < N; ++x) n += nloads(x);
@@ -257,7 +251,7 @@ struct StreamB {
   static constexpr int NL = NL1 + 4 * C::ND;
   static constexpr int load_of(int k) { return k < NB1 ? k / C::DW : NL1 + (k - NB1); }
   static constexpr bool first_use(int k) { return k >= NB1 || k % C::DW == 0; }
-  static constexpr int ninst(int l) { return (l >= NL1 && C::TCOPY) ? 1 : 2; }  // LDS instructions of load l
+  static constexpr int ninst(int) { return 2; }  // LDS instructions of a load (two transposing halves)
   // last load issued before MFMA k runs
   static constexpr int issued_by(int k, int pf) {
     const int x = load_of(k) + pf;
@@ -545,7 +539,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   const int w_swz = swz_f<C::NCH_S>(w_row);
   const int oW = C::OFF_DS + w_row * C::PS + 8 * g;
   const int oL = C::OFF_LD + (C::QW * wq + 4 * g) * 4;                           // row terms (buffer-relative)
-  const int oQT = C::OFF_QT + c32 * C::PT + g * 16 + C::QW * wq * 2;              // Q^T, dO^T fragments (TCOPY)
   // dQ accumulator, fragment order: 32 x 32 blocks of 4 KB; inside a block,
   // register group h (rows 8h + 4g .. + 3, column lane%32) of every lane is
   // one 1 KB run, lane-major, 16 bytes per lane. A wave's block mb starts at
@@ -562,22 +555,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   int goffQ[C::DMA_QW];
 #pragma unroll
   for (int x = 0; x < C::DMA_QW; ++x) goffQ[x] = dma_goff<C::NCH>(w + 4 * x, lane);
-  // transposed tiles: D rows of BQ elements, S elements apart in global memory
-  int goffT[C::TCOPY ? C::DMA_TW : 1];
-  if constexpr (C::TCOPY) {
-#pragma unroll
-    for (int x = 0; x < C::DMA_TW; ++x) {
-      const int p = (w + 4 * x) * 64 + lane;
-      const int row = p / (C::NCT + 1), col = p % (C::NCT + 1);
-      goffT[x] = row * a.S * 2 + (col < C::NCT ? col : 0) * 16;
-    }
-  }
-  int goffT_last = 0;  // the last transposed-tile instruction (repeated by waves with fewer)
-  if constexpr (C::TCOPY) {
-    const int p = (C::DMA_T - 1) * 64 + lane;
-    const int row = p / (C::NCT + 1), col = p % (C::NCT + 1);
-    goffT_last = row * a.S * 2 + (col < C::NCT ? col : 0) * 16;
-  }
 
   int ring_id = 0, slot = 0;
   if (!a.ticket_mode) {
@@ -618,18 +595,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       if (ins < C::DMA_Q) {
         dma16(gq + (uint32_t)goffQ[x], base + ins * 1024);
         dma16(gd + (uint32_t)goffQ[x], base + C::QB + ins * 1024);
-      }
-    }
-    if constexpr (C::TCOPY) {
-      const unsigned char* gqt = reinterpret_cast<const unsigned char*>(a.qt + head_off + qrow0);
-      const unsigned char* gdt = reinterpret_cast<const unsigned char*>(a.dot + head_off + qrow0);
-#pragma unroll
-      for (int x = 0; x < C::DMA_TW; ++x) {
-        const int ins = w + 4 * x;
-        if (ins < C::DMA_T) {
-          dma16(gqt + (uint32_t)goffT[x], base + C::OFF_QT + ins * 1024);
-          dma16(gdt + (uint32_t)goffT[x], base + C::OFF_QT + C::QTB + ins * 1024);
-        }
       }
     }
     float* ld = reinterpret_cast<float*>(base + C::OFF_LD);
@@ -777,13 +742,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
           const __bf16* src = (u & 1) ? a.dout : a.q;
           dma16(reinterpret_cast<const unsigned char*>(src + head_off + nrow0 * D) + (uint32_t)go,
                 nbase + ((u & 1) ? C::QB : 0) + ins * 1024);
-        } else if constexpr (C::TCOPY && u < 2 * C::DMA_QW + 2 * C::DMA_TW) {
-          constexpr int v = u - 2 * C::DMA_QW, x = v / 2;
-          const int ins = w + 4 * x < C::DMA_T ? w + 4 * x : C::DMA_T - 1;
-          const int go = w + 4 * x < C::DMA_T ? goffT[x] : goffT_last;
-          const __bf16* src = (v & 1) ? a.dot : a.qt;
-          dma16(reinterpret_cast<const unsigned char*>(src + head_off + nrow0) + (uint32_t)go,
-                nbase + C::OFF_QT + ((v & 1) ? C::QTB : 0) + ins * 1024);
         } else {
           // row terms: waves 0, 2 load -LSE/scale, waves 1, 3 load -D (duplicates write the same bytes)
           float* ld = reinterpret_cast<float*>(nbase + C::OFF_LD) + (w & 1) * BQ;
@@ -799,7 +757,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       int seen = rk;  // the flag as last read (read in stream A)
       const int vb = C::OFF_B0 + b * C::BUF;
       const int vL = oL + vb;
-      const uint32_t aA = lbase + oA + vb, aT = lbase + oT + vb, aQT = lbase + oQT + vb;
+      const uint32_t aA = lbase + oA + vb, aT = lbase + oT + vb;
 
       // ---- accumulator initial values: -LSE/scale (S), -D (dP); mask on diagonal tiles ----
       f32x16 sAcc[C::MQ], pAcc[C::MQ];
@@ -842,21 +800,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
         else if constexpr (kind == 1) o.q = lds_ld16_asm<C::QB + 32 * m * C::PD + 32 * st>(aA);
         else {
           constexpr int sq = 2 * m + st / C::ND, n = st % C::ND;
-          if constexpr (C::TCOPY) {
-            // row d = 32n + lane%32 of Q^T / dO^T, Q positions 16sq + 8g .. +7
-            o.q = lds_ld16_asm<(kind == 2 ? C::QTB : 0) + 32 * n * C::PT + 32 * sq>(aQT);
-          } else {
-            constexpr int off = (kind == 2 ? C::QB : 0) + 16 * sq * C::PD + 64 * n;
-            o.lo = lds_tr_asm<off>(aT);
-            o.hi = lds_tr_asm<off + 2 * C::PD>(aT);
-          }
+          constexpr int off = (kind == 2 ? C::QB : 0) + 16 * sq * C::PD + 64 * n;
+          o.lo = lds_tr_asm<off>(aT);
+          o.hi = lds_tr_asm<off + 2 * C::PD>(aT);
         }
       };
       // wait for MFMA k's operand (N = own loads issued after it) and return it
       auto waitA = [&](auto kc, Opnd& o) -> u32x4 {
         constexpr int k = decltype(kc)::value;
         constexpr int N = SA::loads_after(k, PF);
-        if constexpr (SA::sdp(k) || C::TCOPY) {
+        if constexpr (SA::sdp(k)) {
           lgkm_wait<N>(o.q);
           return o.q;
         } else {
@@ -930,9 +883,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
         if constexpr (k + PF < SA::N) loadA(std::integral_constant<int, k + PF>{}, ring[(k + PF) % RING]);
         // operands are awaited in pairs: the even MFMA's wait also covers the
         // next one, which then needs neither a wait nor a hazard gap
-        constexpr bool q0 = SA::sdp(k) || C::TCOPY;
+        constexpr bool q0 = SA::sdp(k);
         if constexpr (k % 2 == 0 && k + 1 < SA::N) {
-          constexpr bool q1 = SA::sdp(k + 1) || C::TCOPY;
+          constexpr bool q1 = SA::sdp(k + 1);
           lgkm_wait2<SA::loads_after(k + 1, PF - 1), q0, q1>(ring[k % RING], ring[(k + 1) % RING]);
           mfmaA(kc, q0 ? ring[k % RING].q : cat2(ring[k % RING].lo, ring[k % RING].hi));
         } else if constexpr (k % 2 == 1) {
@@ -1004,13 +957,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
         } else {
           constexpr int x = l - SB_::NL1, kind = 2 + (x & 1), st = x >> 1;
           constexpr int sq = 2 * (C::MQ - 1) + st / C::ND, n = st % C::ND;
-          if constexpr (C::TCOPY) {
-            o.q = lds_ld16_asm<(kind == 2 ? C::QTB : 0) + 32 * n * C::PT + 32 * sq>(aQT);
-          } else {
-            constexpr int off = (kind == 2 ? C::QB : 0) + 16 * sq * C::PD + 64 * n;
-            o.lo = lds_tr_asm<off>(aT);
-            o.hi = lds_tr_asm<off + 2 * C::PD>(aT);
-          }
+          constexpr int off = (kind == 2 ? C::QB : 0) + 16 * sq * C::PD + 64 * n;
+          o.lo = lds_tr_asm<off>(aT);
+          o.hi = lds_tr_asm<off + 2 * C::PD>(aT);
         }
       };
       auto mfmaB = [&](auto kc, const u32x4& opr) {
@@ -1185,19 +1134,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
         constexpr int l = SB_::load_of(k);
         Opnd& o = ring[l % RING];
         // operands are awaited in pairs of loads (l even: l and l + 1)
-        constexpr bool qo = k >= NB1 && C::TCOPY;
         if constexpr (SB_::first_use(k) && l % 2 == 0) {
-          if constexpr (l + 1 < SB_::NL) {
-            constexpr bool q1 = l + 1 >= SB_::NL1 && C::TCOPY;
-            lgkm_wait2<SB_::insts_after(k, PF) - SB_::ninst(l + 1), qo, q1>(o, ring[(l + 1) % RING]);
-          } else if constexpr (qo) {
-            lgkm_wait<SB_::insts_after(k, PF)>(o.q);
-          } else {
+          if constexpr (l + 1 < SB_::NL)
+            lgkm_wait2<SB_::insts_after(k, PF) - SB_::ninst(l + 1), false, false>(o, ring[(l + 1) % RING]);
+          else
             lgkm_wait<SB_::insts_after(k, PF)>(o.lo, o.hi);
-          }
         }
-        if constexpr (qo) mfmaB(kc, o.q);
-        else mfmaB(kc, cat2(o.lo, o.hi));
+        mfmaB(kc, cat2(o.lo, o.hi));
         DETATTN_FENCE();
       });
 

@@ -232,16 +232,6 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
                             nlse, ndelta, rows, flags,
                             BH * P.pub.n_q, header, unordered ? dqacc : nullptr, elems, st_);
   if (e != hipSuccess) return DETATTN_ERR_HIP;
-  __bf16* qt = reinterpret_cast<__bf16*>(ws + L.qt_off);
-  __bf16* dot = reinterpret_cast<__bf16*>(ws + L.dot_off);
-  {
-    const MainInfo info = main_info(s.D, P.pub.block_q, P.pub.block_kv, P.causal, P.dqm_internal, false);
-    if (info.tcopy) {
-      e = launch_transpose(s.D, static_cast<const __bf16*>(q), static_cast<const __bf16*>(dout), qt, dot, BH, s.S, st_);
-      if (e != hipSuccess) return DETATTN_ERR_HIP;
-    }
-  }
-
   MainLaunch M;
   std::memset(&M, 0, sizeof(M));
   BwdArgs& a = M.args;
@@ -249,8 +239,6 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
   a.k = static_cast<const __bf16*>(k);
   a.v = static_cast<const __bf16*>(v);
   a.dout = static_cast<const __bf16*>(dout);
-  a.qt = qt;
-  a.dot = dot;
   a.nlse = nlse;
   a.ndelta = ndelta;
   a.dqacc = dqacc;

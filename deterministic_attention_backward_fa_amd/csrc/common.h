@@ -220,7 +220,7 @@ struct WsLayout {
   static constexpr size_t kHeader = 256;         // ticket @0, error word @64, error detail @128
   static constexpr size_t kFlagStride = 128;     // one L2 line per dQ tile flag
   static constexpr size_t kMinBlockQ = 64;
-  size_t flags_off, flags_bytes, ndelta_off, row_bytes, nlse_off, dqacc_off, dqacc_bytes, qt_off, dot_off, total;
+  size_t flags_off, flags_bytes, ndelta_off, row_bytes, nlse_off, dqacc_off, dqacc_bytes, total;
   __host__ __device__ WsLayout(long long BH, long long S, long long D) {
     flags_off = kHeader;
     long long nq_max = (S + (long long)kMinBlockQ - 1) / (long long)kMinBlockQ;
@@ -230,9 +230,7 @@ struct WsLayout {
     nlse_off = align(ndelta_off + row_bytes);     // -LSE / scale per row
     dqacc_off = align(nlse_off + row_bytes);
     dqacc_bytes = (size_t)(BH * S * D) * 4;
-    qt_off = align(dqacc_off + dqacc_bytes);      // Q per head as [D][S] (bf16, see bwd_transpose_kernel)
-    dot_off = align(qt_off + (size_t)(BH * S * D) * 2);  // dO per head as [D][S]
-    total = align(dot_off + (size_t)(BH * S * D) * 2);
+    total = align(dqacc_off + dqacc_bytes);
   }
   __host__ __device__ static size_t align(size_t x) { return (x + 255) & ~(size_t)255; }
 };

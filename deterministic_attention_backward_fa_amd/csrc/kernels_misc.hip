@@ -74,16 +74,6 @@ hipError_t launch_pre(int D, const __bf16* o, const __bf16* dout, const float* l
   return hipGetLastError();
 }
 
-hipError_t launch_transpose(int D, const __bf16* q, const __bf16* dout, __bf16* qt, __bf16* dot, long long BH, int S,
-                            hipStream_t st) {
-  const dim3 grid((unsigned)(S / 64), (unsigned)BH);
-  if (D == 64)
-    bwd_transpose_kernel<64><<<grid, dim3(256), 0, st>>>(q, dout, qt, dot, S);
-  else
-    bwd_transpose_kernel<128><<<grid, dim3(256), 0, st>>>(q, dout, qt, dot, S);
-  return hipGetLastError();
-}
-
 hipError_t launch_convert(int D, const float* acc, __bf16* dq, long long rows, float scale, bool fragment_order,
                           hipStream_t st) {
   if (!fragment_order) {

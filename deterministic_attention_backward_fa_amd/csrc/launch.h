@@ -21,7 +21,6 @@ struct MainInfo {
   const void* func;  // kernel symbol, or nullptr if the combination is not built
   int lds_bytes;
   int occupancy;     // workgroups per compute unit (0 if unknown)
-  int tcopy;         // the instance reads the transposed Q, dO copies (bwd_transpose_kernel)
 };
 
 MainInfo main_info_d64(int BQ, int BKV, int causal, int dq_mode);
@@ -34,15 +33,13 @@ MainInfo main_info_d128_trace(int BQ, int BKV, int causal, int dq_mode);
 inline MainInfo main_info(int D, int BQ, int BKV, int causal, int dq_mode, bool trace) {
   if (D == 64) return trace ? main_info_d64_trace(BQ, BKV, causal, dq_mode) : main_info_d64(BQ, BKV, causal, dq_mode);
   if (D == 128) return trace ? main_info_d128_trace(BQ, BKV, causal, dq_mode) : main_info_d128(BQ, BKV, causal, dq_mode);
-  return MainInfo{nullptr, 0, 0, 0};
+  return MainInfo{nullptr, 0, 0};
 }
 
 hipError_t launch_pre(int D, const __bf16* o, const __bf16* dout, const float* lse, float inv_scale, float* nlse,
                       float* ndelta,
                       long long rows, int* flags,
                       long long n_flags, unsigned* header, float* dqacc, long long dqacc_elems, hipStream_t st);
-hipError_t launch_transpose(int D, const __bf16* q, const __bf16* dout, __bf16* qt, __bf16* dot, long long BH, int S,
-                            hipStream_t st);
 // fragment_order: the accumulator layout of the read-modify-write dQ modes
 // (dqacc_index); otherwise row-major (atomic modes)
 hipError_t launch_convert(int D, const float* acc, __bf16* dq, long long rows, float scale, bool fragment_order,
