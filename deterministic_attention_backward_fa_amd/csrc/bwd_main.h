@@ -83,7 +83,7 @@
 #define DETATTN_DMA_SPAN 4
 #endif
 #ifndef DETATTN_PUB_AT
-#define DETATTN_PUB_AT 4
+#define DETATTN_PUB_AT 8
 #endif
 #ifndef DETATTN_FLAG_AT
 #define DETATTN_FLAG_AT 7
@@ -98,7 +98,7 @@
 #define DETATTN_ST_AT 0
 #endif
 #ifndef DETATTN_ST_SPAN
-#define DETATTN_ST_SPAN 4
+#define DETATTN_ST_SPAN 8
 #endif
 
 namespace detattn {
@@ -1111,14 +1111,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
           static_for<0, NLD>([&](auto xc) {
             constexpr int x = decltype(xc)::value;
             if constexpr (st_at(x) == k) {
-              if constexpr (x == 0) {
-                // every read has landed (only reads are in flight before the
-                // first write, so one full wait covers them all)
-                static_for<0, NLD>([&](auto yc) {
-                  constexpr int y = decltype(yc)::value;
-                  vm_wait_tied<0>(old[y / 4][y % 4]);
-                });
-              }
+              // read x has landed once at most NLD - 1 later operations are in
+              // flight (reads x+1.., writes ..x-1): vector-memory operations
+              // complete in issue order. On the late path every read was
+              // awaited already.
+              vm_wait_tied<NLD - 1>(old[x / 4][x % 4]);
               dq_store4(x / 4, x % 4, old[x / 4][x % 4] + acc4(x / 4, x % 4));
               if constexpr (x == NLD - 1) adds_finish();
             }
