@@ -36,7 +36,7 @@ class BwdOptions(ctypes.Structure):
                 ("xcd_remap", ctypes.c_int32), ("dq_mode", ctypes.c_int32), ("debug_delay_seed", ctypes.c_uint32),
                 ("timeout_us", ctypes.c_uint32), ("debug_skip_signal", ctypes.c_int32),
                 ("main_begin_event", ctypes.c_void_p), ("main_end_event", ctypes.c_void_p),
-                ("trace", ctypes.c_void_p), ("trace_records", ctypes.c_int32)]
+                ("trace", ctypes.c_void_p), ("trace_records", ctypes.c_int32), ("ring_size", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -78,6 +78,8 @@ def lib():
         ip = ctypes.POINTER(ctypes.c_int32)
         L.detattn_schedule_item.argtypes = [i32, i32, i32, i32, i32, ip, ip, ip, i32]
         L.detattn_schedule_item.restype = ctypes.c_int
+        L.detattn_schedule_item_ring.argtypes = [i32, i32, i32, i32, i32, i32, ip, ip, ip, i32]
+        L.detattn_schedule_item_ring.restype = ctypes.c_int
         L.detattn_schedule_items_per_head.argtypes = [i32, i32, i32, i32]
         L.detattn_schedule_items_per_head.restype = ctypes.c_int
         _lib = L
@@ -120,11 +122,12 @@ def _check_tensor(name, t, dtype, shape):
 
 
 def _options(block_q=0, block_kv=0, grid=0, xcd_remap=None, dq_mode="default", debug_delay_seed=0, timeout_us=0,
-             debug_skip_signal=0, main_begin_event=None, main_end_event=None, trace=None, trace_records=0):
+             debug_skip_signal=0, main_begin_event=None, main_end_event=None, trace=None, trace_records=0,
+             ring_size=0):
     xr = 0 if xcd_remap is None else (1 if xcd_remap else 2)
     return BwdOptions(int(block_q), int(block_kv), int(grid), xr, DQ_MODES[dq_mode], int(debug_delay_seed),
                       int(timeout_us), int(debug_skip_signal), main_begin_event, main_end_event,
-                      trace.data_ptr() if trace is not None else None, int(trace_records))
+                      trace.data_ptr() if trace is not None else None, int(trace_records), int(ring_size))
 
 
 def detattn_fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
@@ -164,7 +167,7 @@ def alloc_workspace(B, H, S, D, device="cuda"):
 def attn_bwd_deterministic(q, k, v, o, dout, lse, causal=False, schedule="serial_ascending", scale=None,
                            workspace=None, out=None, stream=None, **opts):
     """dQ, dK, dV (bf16) of softmax attention. `opts` are BwdOptions fields
-    (block_q, block_kv, grid, xcd_remap, dq_mode, debug_delay_seed, timeout_us, debug_skip_signal)."""
+    (block_q, block_kv, grid, xcd_remap, dq_mode, debug_delay_seed, timeout_us, debug_skip_signal, ring_size)."""
     B, H, S, D = q.shape
     for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
         _check_tensor(n, t, torch.bfloat16, (B, H, S, D))
@@ -194,15 +197,16 @@ def detattn_device_status(workspace, stream=None) -> int:
     return int(lib().detattn_device_status(_ptr(workspace), _stream(stream)))
 
 
-def detattn_schedule_item(schedule, causal, n_q, n_kv, item):
-    """[(q_tile, kv_tile, rank), ...] of one item, from the library's own schedule functions."""
+def detattn_schedule_item(schedule, causal, n_q, n_kv, item, ring=0):
+    """[(q_tile, kv_tile, rank), ...] of one item, from the library's own schedule
+    functions; `ring` = workgroups per ring of the shift schedules (0 = one round)."""
     mask = 1 if causal else 0
-    n = lib().detattn_schedule_item(SCHEDULES[schedule], mask, n_q, n_kv, item, None, None, None, 0)
+    n = lib().detattn_schedule_item_ring(SCHEDULES[schedule], mask, n_q, n_kv, ring, item, None, None, None, 0)
     if n < 0:
-        raise DetAttnError(1, "detattn_schedule_item")
+        raise DetAttnError(1, "detattn_schedule_item_ring")
     arr = (ctypes.c_int32 * max(n, 1))
     qi, kj, rk = arr(), arr(), arr()
-    lib().detattn_schedule_item(SCHEDULES[schedule], mask, n_q, n_kv, item, qi, kj, rk, n)
+    lib().detattn_schedule_item_ring(SCHEDULES[schedule], mask, n_q, n_kv, ring, item, qi, kj, rk, n)
     return [(qi[t], kj[t], rk[t]) for t in range(n)]
 
 

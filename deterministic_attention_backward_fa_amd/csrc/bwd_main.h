@@ -615,7 +615,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     }
   };
 
-  for (long long round = 0;; ++round) {
+  // Ring mode: the ring takes heads ring_id, ring_id + rings, ...; inside a
+  // head, workgroup `slot` takes items slot, G + slot, ... (one per round,
+  // G = a.ring workgroups per ring).
+  int ring_bh = ring_id, ring_it = slot;
+  for (;;) {
     long long gidx;
     if (a.ticket_mode) {
       if (tid == 0) sMisc[0] = (int)atomicAdd(a.ticket, 1u);
@@ -624,9 +628,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       __syncthreads();
       if (gidx >= total_items) return;
     } else {
-      const long long bh = (long long)ring_id + round * a.rings;
-      if (bh >= a.BH) return;
-      gidx = bh * ipH + slot;
+      if (ring_bh >= a.BH) return;
+      gidx = (long long)ring_bh * ipH + ring_it;
+      ring_it += a.ring;
+      if (ring_it >= ipH) {
+        ring_it = slot;
+        ring_bh += a.rings;
+      }
     }
     const int bh = (int)(gidx / ipH);
     const int it = (int)(gidx % ipH);

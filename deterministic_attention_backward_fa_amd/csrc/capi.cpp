@@ -52,6 +52,20 @@ bool tiles_built(int D, int bq, int bkv) {
   return false;
 }
 
+// Workgroups of one XCD on MI355X (256 compute units in 8 XCDs).
+constexpr int kXcdSlots = 32;
+
+// Default ring size of the shift schedules: the head's items if they fit one
+// XCD, else the largest divisor of the item count that does (the ring then
+// takes the items in rounds). It depends on the shape only, so the
+// accumulation order, and with it every bit of dQ, does not depend on the grid.
+int default_ring(int items_per_head) {
+  if (items_per_head <= kXcdSlots) return items_per_head;
+  for (int g = kXcdSlots; g > 1; --g)
+    if (items_per_head % g == 0) return g;
+  return 1;
+}
+
 int device_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
@@ -62,6 +76,7 @@ int device_cus() {
 struct Plan {
   detattn_plan_t pub;
   int causal, sch, dqm_internal, xcd;
+  Sched sc;
   long long timeout_ticks;
 };
 
@@ -75,7 +90,7 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
   std::memset(&o, 0, sizeof(o));
   if (opt) o = *opt;
   if (o.block_q < 0 || o.block_kv < 0 || o.grid < 0 || o.xcd_remap < 0 || o.xcd_remap > 2 || o.dq_mode < 0 ||
-      o.dq_mode > 3)
+      o.dq_mode > 3 || o.ring_size < 0)
     return DETATTN_ERR_INVALID_ARG;
   int bq, bkv;
   default_tiles(s.D, s.S, bq, bkv);
@@ -93,7 +108,13 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
   const MainInfo info0 = main_info(s.D, bq, bkv, causal, kDqOrderedRmw, false);
   if (!info0.func) return DETATTN_ERR_UNSUPPORTED;
 
-  const Sched sc{(int)sch, causal, n_q, n_kv, r};
+  const bool ring_sched = (sch == DETATTN_SHIFT || sch == DETATTN_SYMMETRIC_SHIFT);
+  Sched sc{(int)sch, causal, n_q, n_kv, r, 0};
+  if (ring_sched) {
+    const int ip = sc.items_per_head();
+    sc.G = o.ring_size ? o.ring_size : default_ring(ip);
+    if (ip % sc.G != 0) return DETATTN_ERR_UNSUPPORTED;
+  }
   const long long BH = (long long)s.B * s.H;
   const long long items = BH * sc.items_per_head();
   int capacity = 0;  // co-resident workgroups
@@ -103,15 +124,15 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
     if (cus <= 0 || info0.occupancy <= 0) return DETATTN_ERR_HIP;
     capacity = cus * info0.occupancy;
   }
-  const bool ring_sched = (sch == DETATTN_SHIFT || sch == DETATTN_SYMMETRIC_SHIFT);
   int grid = o.grid ? o.grid : capacity;
   int ring = 0, rings = 0;
   int xcd = o.xcd_remap != 2;
   if (ring_sched) {
-    // Every ring (the items of one head) must be co-resident. With the XCD
-    // remap a ring occupies consecutive slots of one XCD (workgroup w runs on
-    // XCD w % 8), so its dQ hand-offs stay inside that XCD's L2.
-    ring = sc.items_per_head();
+    // Every ring (G workgroups sharing one head's items) must be co-resident.
+    // With the XCD remap a ring occupies consecutive slots of one XCD
+    // (workgroup w runs on XCD w % 8), so its dQ hand-offs stay inside that
+    // XCD's L2.
+    ring = sc.G;
     if (grid < ring) return DETATTN_ERR_UNSUPPORTED;
     if (xcd && grid % 8 == 0 && ring <= grid / 8) {
       long long per_xcd = (grid / 8) / ring;
@@ -155,6 +176,7 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
   P.pub.cooperative = ring_sched ? 1 : 0;
   P.causal = causal;
   P.sch = (int)sch;
+  P.sc = sc;
   P.dqm_internal = dqm;
   P.xcd = xcd;
   const long long us = o.timeout_us ? (long long)o.timeout_us : 4000000LL;
@@ -250,7 +272,7 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
   a.BH = (int)BH;
   a.S = s.S;
   a.scale = s.softmax_scale;
-  a.sc = Sched{P.sch, P.causal, P.pub.n_q, P.pub.n_kv, P.pub.block_kv / P.pub.block_q};
+  a.sc = P.sc;
   a.ticket_mode = P.pub.ring == 0;
   a.ring = P.pub.ring;
   a.rings = P.pub.rings;
@@ -320,17 +342,21 @@ int detattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse
 int detattn_schedule_items_per_head(int32_t schedule, int32_t mask, int32_t n_q, int32_t n_kv) {
   if (schedule < 0 || schedule > 4 || (mask != 0 && mask != 1) || n_q <= 0 || n_kv <= 0 || n_q % n_kv != 0)
     return -1;
+  const int r = n_q / n_kv;
+  if (r != 1 && r != 2 && r != 4 && r != 8) return -1;  // tiles are powers of two
   if (schedule == kShift && mask != 0) return -1;
   if (schedule == kSymmetricShift && (mask != 1 || n_kv % 2 != 0)) return -1;
-  const Sched sc{schedule, mask, n_q, n_kv, n_q / n_kv};
+  const Sched sc{schedule, mask, n_q, n_kv, n_q / n_kv, 0};
   return sc.items_per_head();
 }
 
-int detattn_schedule_item(int32_t schedule, int32_t mask, int32_t n_q, int32_t n_kv, int32_t item, int32_t* q_tiles,
-                          int32_t* kv_tiles, int32_t* ranks, int32_t cap) {
+int detattn_schedule_item_ring(int32_t schedule, int32_t mask, int32_t n_q, int32_t n_kv, int32_t ring,
+                               int32_t item, int32_t* q_tiles, int32_t* kv_tiles, int32_t* ranks, int32_t cap) {
   const int ip = detattn_schedule_items_per_head(schedule, mask, n_q, n_kv);
-  if (ip < 0 || item < 0 || item >= ip || cap < 0) return -1;
-  const Sched sc{schedule, mask, n_q, n_kv, n_q / n_kv};
+  if (ip < 0 || item < 0 || item >= ip || cap < 0 || ring < 0) return -1;
+  const bool ring_sched = schedule == kShift || schedule == kSymmetricShift;
+  if (ring > 0 && (!ring_sched || ip % ring != 0)) return -1;
+  const Sched sc{schedule, mask, n_q, n_kv, n_q / n_kv, ring};
   const int len = sc.item_len(item);
   // the incremental walk the device takes, checked step by step against the
   // closed forms tile() and rank()
@@ -350,6 +376,11 @@ int detattn_schedule_item(int32_t schedule, int32_t mask, int32_t n_q, int32_t n
     }
   }
   return len;
+}
+
+int detattn_schedule_item(int32_t schedule, int32_t mask, int32_t n_q, int32_t n_kv, int32_t item, int32_t* q_tiles,
+                          int32_t* kv_tiles, int32_t* ranks, int32_t cap) {
+  return detattn_schedule_item_ring(schedule, mask, n_q, n_kv, 0, item, q_tiles, kv_tiles, ranks, cap);
 }
 
 }  // extern "C"

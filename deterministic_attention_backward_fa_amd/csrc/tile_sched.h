@@ -22,6 +22,15 @@
 //   gist.science 2.2B; the fold itself is this library's reading, as the pages
 //   give no figure). The order is the step order.
 // * atomic (non-deterministic): ascending visits, unordered atomic adds.
+//
+// Rings of the two shift schedules. The pages' model has one SM per item, all
+// in lock step. Here a ring of G workgroups may hold fewer workgroups than a
+// head has items: workgroup g then takes items g, G + g, 2G + g, ... in rounds,
+// each round right after its previous item. A dQ tile's order is round-major
+// and, inside a round, the step order (the lock-step order of that round's G
+// items, which are conflict-free as a subset of all items). G = items per head
+// is the pages' single round. With G = 32 a ring fits one XCD of MI355X, which
+// keeps its dQ hand-offs in that XCD's L2 at any sequence length.
 #pragma once
 
 namespace detattn {
@@ -31,31 +40,40 @@ namespace detattn {
 // per-tile bookkeeping needs no division. Sched::walk positions a walk at
 // the segment's first step; advance(t) moves it to step t (the next one).
 // Every schedule's segment is an arithmetic run of Q tiles with at most one
-// wrap-around and at most one jump, and its ranks are either the KV tile
-// itself or a step counter divided by r (shift orders).
+// wrap-around and at most one jump. A rank is either fixed (the KV tile) or,
+// for the shift orders, a function of q, the steps since the segment (or the
+// jump) began divided by r, and of the Q tile:
+//   rank = base + min(q, c1) + max(0, q - c2) + max(0, e0 + i / r);
+// a fixed rank is base alone (c1 = 0, the other terms vanish).
+// With one round (G = items per head) this is q; the other terms count the
+// contributions of earlier rounds and the round's own wrap-around.
 struct SegWalk {
+  static constexpr int kBig = 1 << 28;
   int i;                // Q tile of the current step
-  int rank;             // rank of the current step (when ranked by step)
-  int cnt;              // steps taken in the current group of r steps
+  int n;                // steps since the segment (or the jump) began; q = n >> rs
   int di;               // Q tile increment per step (+1 or -1)
   int wrap_at, wrap_to; // a step reaching Q tile wrap_at continues at wrap_to
-  int jump_t, jump_i;   // step jump_t continues at Q tile jump_i, ranks restart at 0
-  int r;                // steps per rank (shift orders)
-  int fixed_rank;       // the rank of every step, or -1 when ranked by step
+  int jump_t, jump_i;   // step jump_t continues at Q tile jump_i, n restarts at 0
+  int rs;               // log2(r)
+  int base, c1, c2, e0; // rank terms; a fixed rank is base with c1 = 0
 
-  __host__ __device__ __forceinline__ int rank_now() const { return fixed_rank >= 0 ? fixed_rank : rank; }
+  __host__ __device__ __forceinline__ int rank_now() const {
+    const int q = n >> rs;
+    const int lo = q < c1 ? q : c1;
+    const int over = q - c2 > 0 ? q - c2 : 0;
+    const int late = e0 + (i >> rs) > 0 ? e0 + (i >> rs) : 0;
+    return base + lo + over + late;
+  }
 
   __host__ __device__ __forceinline__ void advance(int t) {
     i += di;
     if (i == wrap_at) i = wrap_to;
-    ++cnt;
-    const bool next_group = cnt == r;
-    cnt = next_group ? 0 : cnt;
-    rank += next_group ? 1 : 0;
+    ++n;
     if (t == jump_t) {
       i = jump_i;
-      rank = 0;
-      cnt = 0;
+      n = 0;
+      c2 = kBig;
+      e0 = -kBig;
     }
   }
 };
@@ -64,10 +82,13 @@ enum Schedule : int { kSerialAscending = 0, kDescendingQ = 1, kShift = 2, kSymme
 
 struct Sched {
   int sch, causal, n_q, n_kv, r;
+  int G;  // ring size of the shift schedules (items per round); 0 = items per head (one round)
 
   __host__ __device__ __forceinline__ int items_per_head() const {
     return sch == kSymmetricShift ? n_kv / 2 : n_kv;
   }
+  __host__ __device__ __forceinline__ int ring() const { return G > 0 ? G : items_per_head(); }
+  __host__ __device__ __forceinline__ int log2r() const { return r == 1 ? 0 : r == 2 ? 1 : r == 4 ? 2 : 3; }
 
   __host__ __device__ __forceinline__ int item_len(int it) const {
     switch (sch) {
@@ -129,24 +150,31 @@ struct Sched {
   // segment's KV tile. Equal, step by step, to tile() and rank().
   __host__ __device__ __forceinline__ SegWalk walk(int it, int seg, int& j) const {
     SegWalk w;
-    w.rank = 0;
-    w.cnt = 0;
+    w.n = 0;
     w.di = 1;
     w.wrap_at = n_q + 1;  // not reached
     w.wrap_to = 0;
     w.jump_t = -1;        // no jump
     w.jump_i = 0;
-    w.r = r;
-    w.fixed_rank = -1;
+    w.rs = log2r();
+    const int Gr = ring();
+    const int kG = it - it % Gr, g = it % Gr;  // round start and slot
+    w.base = kG;
+    w.c1 = Gr - 1 - g;
+    w.c2 = SegWalk::kBig;
+    w.e0 = -SegWalk::kBig;
     switch (sch) {
       case kShift:
         j = it;
         w.i = (it * r) % n_q;
         w.wrap_at = n_q;
         w.wrap_to = 0;
+        w.c2 = n_kv - 1 - g;
         break;
       case kSymmetricShift: {
         const int half = n_q / 2;
+        const int P = n_kv / 2;
+        w.e0 = kG - n_kv + 1;  // bottom-half rows: bottom-branch adds of earlier rounds
         if (seg == 0) {  // phase 1 over rows half.., then column it upward from row it*r
           j = it;
           w.i = half + (it * r) % half;
@@ -154,12 +182,14 @@ struct Sched {
           w.wrap_to = half;
           w.jump_t = half;
           w.jump_i = it * r;
-        } else {         // column n_kv-1-it downward from the last row
+          w.c2 = P - 1 - g;
+        } else {         // column n_kv-1-it downward from the last row, after the round's phase 1
           j = n_kv - 1 - it;
           w.i = n_q - 1;
           w.di = -1;
           w.wrap_at = -2;
-          w.fixed_rank = j;
+          w.base = kG + 2 * Gr - 1 - g;
+          w.c1 = 0;
         }
         break;
       }
@@ -168,34 +198,57 @@ struct Sched {
         w.i = n_q - 1;
         w.di = -1;
         w.wrap_at = -2;
-        w.fixed_rank = j;
+        w.base = j;
+        w.c1 = 0;
         break;
       default:  // serial ascending, atomic
         j = it;
         w.i = causal ? it * r : 0;
-        w.fixed_rank = j;
+        w.base = j;
+        w.c1 = 0;
         break;
     }
     return w;
   }
 
-  // Position of KV tile j in dQ tile i's accumulation order.
+  // Position of KV tile j in dQ tile i's accumulation order, counted
+  // directly: contributions of earlier rounds, then those of the same round
+  // at earlier steps.
   __host__ __device__ __forceinline__ int rank(int i, int j) const {
+    const int Gr = ring();
     switch (sch) {
       case kShift: {
-        int d = (i - j * r) % n_q;
-        if (d < 0) d += n_q;
-        return d / r;
+        const int kG = j - j % Gr, g = j % Gr;
+        int t = (i - j * r) % n_q;
+        if (t < 0) t += n_q;
+        const int q = t / r;
+        // round items at earlier steps: g' > g before the wrap, g' < g after it
+        const int before = q < Gr - 1 - g ? q : Gr - 1 - g;
+        const int wrapped = q - (n_kv - 1 - g) > 0 ? q - (n_kv - 1 - g) : 0;
+        return kG + before + wrapped;
       }
       case kSymmetricShift: {
-        const int half = n_q / 2;
-        if (j >= n_kv / 2) return j;  // phase-2 bottom branch: after all phase-1 adds, ascending j
-        if (i >= half) {              // phase 1 on the dense rectangle
-          int d = (i - half - j * r) % half;
-          if (d < 0) d += half;
-          return d / r;
+        const int half = n_q / 2, P = n_kv / 2;
+        const int u = i / r;
+        if (j >= P) {  // bottom branch of item p = n_kv-1-j: after its round's phase 1, larger p first
+          const int p = n_kv - 1 - j, kG = p - p % Gr, g = p % Gr;
+          const int earlier_bottom = kG - (n_kv - 1 - u) > 0 ? kG - (n_kv - 1 - u) : 0;
+          return kG + earlier_bottom + Gr + (Gr - 1 - g);
         }
-        return i / r - j;  // phase-2 top branch: later steps belong to smaller p
+        const int p = j, kG = p - p % Gr, g = p % Gr;
+        if (i >= half) {  // phase 1 on the dense rectangle
+          int t = (i - half - p * r) % half;
+          if (t < 0) t += half;
+          const int q = t / r;
+          const int earlier_bottom = kG - (n_kv - 1 - u) > 0 ? kG - (n_kv - 1 - u) : 0;
+          const int before = q < Gr - 1 - g ? q : Gr - 1 - g;
+          const int wrapped = q - (P - 1 - g) > 0 ? q - (P - 1 - g) : 0;
+          return kG + earlier_bottom + before + wrapped;
+        }
+        // top branch: columns p' <= u contribute, later steps for smaller p'
+        const int earlier = kG < u + 1 ? kG : u + 1;
+        const int last = kG + Gr - 1 < u ? kG + Gr - 1 : u;
+        return earlier + last - p;
       }
       default:
         return j;

@@ -114,6 +114,13 @@ typedef struct {
                                 (s_memtime, phase | tile << 8 | item << 32) at the phase boundaries of each
                                 tile (detattn_trace_phase_t); unused records stay as the caller left them */
   int32_t trace_records;     /* records per workgroup in `trace` */
+  int32_t ring_size;         /* SHIFT / SYMMETRIC_SHIFT: workgroups per ring G, a divisor of the items per head;
+                                0 = default: the items per head if at most 32, else the largest divisor <= 32.
+                                With G below the item count, workgroup g of a ring takes items g, G+g, ... in
+                                rounds, and a dQ tile's order is round-major, step order inside a round
+                                (the pages' schedules are the single round G = items per head). G sets the
+                                accumulation order: results are bit-identical across calls with the same G.
+                                Invalid (UNSUPPORTED) if it does not divide the item count. */
 } detattn_bwd_options_t;
 
 /* Phase ids written into the optional trace (low 8 bits of the second word). */
@@ -133,7 +140,7 @@ typedef struct {
   int32_t block_q, block_kv, n_q, n_kv;
   int32_t items;       /* items over all heads */
   int32_t grid;        /* workgroups launched */
-  int32_t ring;        /* workgroups per co-resident ring (shift schedules), else 0 */
+  int32_t ring;        /* workgroups per co-resident ring G (shift schedules), else 0 */
   int32_t rings;       /* rings running at once, else 0 */
   int32_t dq_mode;     /* resolved detattn_dq_mode_t (0 for ATOMIC_NONDET) */
   int32_t cooperative; /* 1 if launched as a cooperative (co-resident) grid */
@@ -199,7 +206,14 @@ const char* detattn_status_string(int status);
 int detattn_schedule_item(int32_t schedule, int32_t mask, int32_t n_q, int32_t n_kv, int32_t item,
                           int32_t* q_tiles, int32_t* kv_tiles, int32_t* ranks, int32_t cap);
 
-/* Items per head of a schedule (n_kv, or n_kv/2 for SYMMETRIC_SHIFT); -1 if invalid. */
+/* The same for a ring of `ring` workgroups (SHIFT and SYMMETRIC_SHIFT only; 0 = one round, as above):
+ * the item's visits do not change, its ranks are those of the round-major order that
+ * detattn_bwd_options_t.ring_size describes. -1 if `ring` does not divide the item count. */
+int detattn_schedule_item_ring(int32_t schedule, int32_t mask, int32_t n_q, int32_t n_kv, int32_t ring,
+                               int32_t item, int32_t* q_tiles, int32_t* kv_tiles, int32_t* ranks, int32_t cap);
+
+/* Items per head of a schedule (n_kv, or n_kv/2 for SYMMETRIC_SHIFT); -1 if invalid
+ * (including n_q / n_kv not a power of two up to 8). */
 int detattn_schedule_items_per_head(int32_t schedule, int32_t mask, int32_t n_q, int32_t n_kv);
 
 #ifdef __cplusplus

@@ -94,7 +94,7 @@ def items(schedule: str, mask: str, n_q: int, n_kv: int) -> List[List[Tile]]:
     return out
 
 
-def accumulation_order(schedule: str, mask: str, n_q: int, n_kv: int) -> Dict[int, List[int]]:
+def accumulation_order(schedule: str, mask: str, n_q: int, n_kv: int, ring: int = 0) -> Dict[int, List[int]]:
     """dQ tile i -> KV tiles in the order their partials are added.
 
     serial_ascending and descending_q both keep FA3's ascending KV order; the
@@ -103,6 +103,13 @@ def accumulation_order(schedule: str, mask: str, n_q: int, n_kv: int) -> Dict[in
     per step in lock step and the contributions to a dQ tile are added in step
     order, which the pages describe as forming a natural dependency chain with
     no conflicts (zskr.cn section 3.2; gist.science section 2.2B).
+
+    ``ring`` (shift schedules only): the number of workgroups that share a
+    head's items when there are fewer of them than items. The pages' model has
+    one SM per item; this reading extends it: workgroup g takes items g,
+    ring + g, 2 ring + g, ... one round after another, the items of one round
+    run in lock step, and a dQ tile takes its partials round by round, in step
+    order inside a round. 0 (or the item count) is the pages' single round.
     """
     if schedule == "atomic_nondet":
         raise ValueError("atomic_nondet has no fixed accumulation order")
@@ -113,21 +120,25 @@ def accumulation_order(schedule: str, mask: str, n_q: int, n_kv: int) -> Dict[in
         for i in range(n_q):
             order[i] = [j for j in range(n_kv) if tile_visible(i, j, r, causal)]
         return order
-    contrib: Dict[int, List[Tuple[int, int]]] = {i: [] for i in range(n_q)}
-    for seq in items(schedule, mask, n_q, n_kv):
+    seqs = items(schedule, mask, n_q, n_kv)
+    G = ring if ring else len(seqs)
+    if len(seqs) % G != 0:
+        raise ValueError(f"ring {G} does not divide {len(seqs)} items")
+    contrib: Dict[int, List[Tuple[int, int, int]]] = {i: [] for i in range(n_q)}
+    for it, seq in enumerate(seqs):
         for step, (i, j) in enumerate(seq):
-            contrib[i].append((step, j))
+            contrib[i].append((it // G, step, j))
     for i, lst in contrib.items():
-        steps = [s for s, _ in lst]
-        assert len(set(steps)) == len(steps), f"two contributions to dQ tile {i} at one step"
-        order[i] = [j for _, j in sorted(lst)]
+        keys = [(k, s) for k, s, _ in lst]
+        assert len(set(keys)) == len(keys), f"two contributions to dQ tile {i} at one step of one round"
+        order[i] = [j for _, _, j in sorted(lst)]
     return order
 
 
-def rank_table(schedule: str, mask: str, n_q: int, n_kv: int) -> Dict[Tile, int]:
+def rank_table(schedule: str, mask: str, n_q: int, n_kv: int, ring: int = 0) -> Dict[Tile, int]:
     """(i, j) -> position of KV tile j in dQ tile i's accumulation order."""
     out: Dict[Tile, int] = {}
-    for i, js in accumulation_order(schedule, mask, n_q, n_kv).items():
+    for i, js in accumulation_order(schedule, mask, n_q, n_kv, ring).items():
         for pos, j in enumerate(js):
             out[(i, j)] = pos
     return out

@@ -120,7 +120,8 @@ def test_default_tiles_and_rings(cfg):
     p = da.detattn_bwd_plan(B, H, S, D, causal, sched, grid=256)
     assert (p["block_q"], p["block_kv"]) == (bq, bkv)
     n_kv = S // bkv
-    ring = n_kv if sched == "shift" else n_kv // 2
+    items = n_kv if sched == "shift" else n_kv // 2
+    ring = min(items, 32)  # one XCD's workgroups; larger heads take their items in rounds
     assert p["ring"] == ring and p["cooperative"] == 1
     assert p["grid"] == p["rings"] * ring <= 256
     assert p["rings"] >= 1
@@ -155,3 +156,46 @@ def test_library_schedule_matches_oracle(sched, mask, n_kv, r):
         assert [(a, b) for a, b, _ in got] == want
         if ranks is not None:
             assert [c for _, _, c in got] == [ranks[t] for t in want]
+
+
+RING_CASES = [(n_kv, r) for n_kv in (4, 8, 16, 64, 128) for r in (1, 2)]
+
+
+@pytest.mark.parametrize("n_kv,r", RING_CASES)
+@pytest.mark.parametrize("sched,mask", [("shift", "full"), ("symmetric_shift", "causal")])
+def test_library_ring_ranks_match_oracle(sched, mask, n_kv, r):
+    """With a ring of G workgroups the library's ranks (the incremental walk the
+    kernel takes, checked in the library against its counting closed form)
+    equal the oracle's round-major order, for every divisor G of the items."""
+    n_q = n_kv * r
+    causal = mask == "causal"
+    ip = da.detattn_schedule_items_per_head(sched, causal, n_q, n_kv)
+    want_items = OS.items(sched, mask, n_q, n_kv)
+    rings = [g for g in range(1, ip + 1) if ip % g == 0]
+    if n_kv >= 64:
+        rings = [g for g in rings if g in (1, 2, 8, 32, ip)]
+    for G in rings:
+        ranks = OS.rank_table(sched, mask, n_q, n_kv, ring=G)
+        for it, want in enumerate(want_items):
+            got = da.detattn_schedule_item(sched, causal, n_q, n_kv, it, ring=G)
+            assert [(a, b) for a, b, _ in got] == want
+            assert [c for _, _, c in got] == [ranks[t] for t in want], (G, it)
+    bad = [g for g in range(2, ip) if ip % g != 0]
+    for G in bad[:2]:
+        with pytest.raises(da.DetAttnError):
+            da.detattn_schedule_item(sched, causal, n_q, n_kv, 0, ring=G)
+
+
+def test_ring_option_in_plan():
+    """Default rings: a head's items if they fit one XCD (32 workgroups), else
+    the largest divisor <= 32; an explicit ring_size must divide the items."""
+    p = da.detattn_bwd_plan(1, 16, 16384, 128, True, "symmetric_shift", grid=256)
+    assert (p["n_kv"], p["ring"], p["rings"], p["grid"]) == (256, 32, 8, 256)
+    p = da.detattn_bwd_plan(1, 16, 16384, 128, False, "shift", grid=256)
+    assert (p["ring"], p["rings"]) == (32, 8)
+    p = da.detattn_bwd_plan(1, 32, 8192, 128, True, "symmetric_shift", grid=256)
+    assert (p["ring"], p["rings"]) == (32, 8)
+    p = da.detattn_bwd_plan(1, 16, 16384, 128, False, "shift", grid=256, ring_size=256)
+    assert (p["ring"], p["rings"], p["dq_mode"]) == (256, 1, da.DQ_MODES["atomic"])
+    with pytest.raises(da.DetAttnError):
+        da.detattn_bwd_plan(1, 16, 16384, 128, False, "shift", grid=256, ring_size=48)

@@ -144,3 +144,55 @@ def test_timeout_path_reports_and_exits():
     # the next normal call on the same workspace is clean again
     da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=False, schedule="serial_ascending", workspace=ws)
     assert da.detattn_device_status(ws) == 0
+
+
+RING_CASES = [
+    # (B, H, S, D, causal, seed, options, ring sizes): heads with more items than ring workgroups
+    (1, 2, 512, 64, False, 21, {"block_q": 64, "block_kv": 64}, (1, 2, 4)),   # shift, 8 items
+    (1, 2, 512, 128, True, 22, {"block_q": 64, "block_kv": 64}, (1, 2)),      # symmetric, 4 items
+    (1, 2, 1024, 128, True, 23, {}, (1, 2)),                                  # symmetric, r = 2
+    (1, 1, 1024, 128, False, 24, {}, (2, 4)),                                 # shift, r = 2
+]
+
+
+@pytest.mark.parametrize("case", RING_CASES, ids=lambda c: f"B{c[0]}H{c[1]}S{c[2]}D{c[3]}{'c' if c[4] else 'f'}")
+def test_ring_rounds_match_oracle_and_repeat(case):
+    """Rings smaller than the item count (items taken in rounds): oracle parity,
+    repeat and placement invariance at a fixed ring size, and dK/dV independent
+    of the ring size (they never depend on the dQ order)."""
+    B, H, S, D, causal, seed, opts, rings = case
+    sched = "symmetric_shift" if causal else "shift"
+    scale = 1.0 / math.sqrt(D)
+    cpu, (q, k, v, do, o, lse) = inputs(B, H, S, D, seed, causal)
+    dq_r, dk_r, dv_r, _, _ = _oracle(cpu, causal, scale)
+    ws = da.alloc_workspace(B, H, S, D)
+    first_dkdv = None
+    for G in rings:
+        plan = da.detattn_bwd_plan(B, H, S, D, causal, sched, ring_size=G, **opts)
+        assert plan["ring"] == G
+        say(f"[ring rounds] {case[:6]} {sched} ring {G} plan {plan}")
+        base = [t.clone() for t in da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule=sched,
+                                                            workspace=ws, ring_size=G, **opts)]
+        assert da.detattn_device_status(ws) == 0
+        for name, got, want in (("dq", base[0], dq_r), ("dk", base[1], dk_r), ("dv", base[2], dv_r)):
+            e = rel_err(got.float().cpu().numpy(), want)
+            assert e <= TOL, f"ring {G} {name} rel err {e:.3e}"
+        if first_dkdv is None:
+            first_dkdv = base[1:]
+        assert same_bits(first_dkdv[0], base[1]) and same_bits(first_dkdv[1], base[2])
+        out = tuple(torch.empty_like(t) for t in base)
+        for _ in range(9):
+            da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule=sched, workspace=ws, out=out,
+                                      ring_size=G, **opts)
+            assert all(same_bits(a, b) for a, b in zip(base, out)), f"ring {G} repeat"
+        for var in (dict(debug_delay_seed=777), dict(grid=G * 2 + 8), dict(grid=G)):
+            say(f"[ring rounds] ring {G} {var}")
+            got = da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule=sched, workspace=ws,
+                                            ring_size=G, **opts, **var)
+            assert da.detattn_device_status(ws) == 0
+            vplan = da.detattn_bwd_plan(B, H, S, D, causal, sched, ring_size=G, **opts, **var)
+            assert same_bits(base[1], got[1]) and same_bits(base[2], got[2]), var
+            if vplan["dq_mode"] == plan["dq_mode"]:
+                assert same_bits(base[0], got[0]), var
+            else:
+                assert rel_err(got[0].float().cpu().numpy(), base[0].float().cpu().numpy()) <= 1e-2

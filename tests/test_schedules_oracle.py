@@ -85,3 +85,44 @@ def test_invalid_pairs():
     assert not S.valid("symmetric_shift", "causal", 5, 5)
     with pytest.raises(ValueError):
         S.items("shift", "causal", 4, 4)
+
+
+def test_golden_rings_n4():
+    g = GOLDEN["rings"]
+    got = S.accumulation_order("shift", "full", 4, 4, ring=2)
+    assert {str(k): v for k, v in got.items()} == g["shift_full_G2"]["dq_order"]
+    got = S.accumulation_order("symmetric_shift", "causal", 4, 4, ring=1)
+    assert {str(k): v for k, v in got.items()} == g["symmetric_shift_causal_G1"]["dq_order"]
+
+
+@pytest.mark.parametrize("n_kv,r", [(4, 1), (8, 2), (16, 1), (16, 2)])
+def test_ring_orders_reduce_to_plain_cases(n_kv, r):
+    """One item per round orders every dQ tile by item index (inside a
+    symmetric pair: its left column, then its right one); a ring as large as
+    the item count is the pages' single round."""
+    n_q = n_kv * r
+    shift1 = S.accumulation_order("shift", "full", n_q, n_kv, ring=1)
+    assert all(js == list(range(n_kv)) for js in shift1.values())
+    assert S.accumulation_order("shift", "full", n_q, n_kv, ring=n_kv) == S.accumulation_order(
+        "shift", "full", n_q, n_kv)
+    sym1 = S.accumulation_order("symmetric_shift", "causal", n_q, n_kv, ring=1)
+    for i, js in sym1.items():
+        want = []
+        for p in range(n_kv // 2):
+            want += [j for j in (p, n_kv - 1 - p) if S.tile_visible(i, j, r, True)]
+        assert js == want
+    P = n_kv // 2
+    assert S.accumulation_order("symmetric_shift", "causal", n_q, n_kv, ring=P) == S.accumulation_order(
+        "symmetric_shift", "causal", n_q, n_kv)
+
+
+@pytest.mark.parametrize("n_kv,r", [(8, 1), (16, 2), (32, 1)])
+def test_ring_orders_cover_each_contribution_once(n_kv, r):
+    n_q = n_kv * r
+    for sched, mask, ip in (("shift", "full", n_kv), ("symmetric_shift", "causal", n_kv // 2)):
+        for G in [g for g in range(1, ip + 1) if ip % g == 0]:
+            order = S.accumulation_order(sched, mask, n_q, n_kv, ring=G)
+            for i, js in order.items():
+                assert sorted(js) == [j for j in range(n_kv) if S.tile_visible(i, j, r, mask == "causal")]
+    with pytest.raises(ValueError):
+        S.accumulation_order("shift", "full", 12, 12, ring=5)
