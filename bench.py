@@ -171,6 +171,10 @@ def main():
     ap.add_argument("--only-headline", action="store_true", help="skip the other schedules")
     ap.add_argument("--dq-mode", default="default", choices=["default", "rmw", "atomic", "xcd_local"],
                     help="ordered dQ accumulation mechanism for the deterministic schedules")
+    ap.add_argument("--block-q", type=int, default=0, help="Q tile rows (0 = library default)")
+    ap.add_argument("--block-kv", type=int, default=0, help="KV tile rows (0 = library default)")
+    ap.add_argument("--ring-size", type=int, default=0,
+                    help="workgroups per ring of the shift schedules (0 = library default)")
     ap.add_argument("--trace", action="store_true", help="log the headline schedule's per-tile phase breakdown")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
@@ -207,22 +211,29 @@ def main():
         scheds += [s for s in (["serial_ascending", "descending_q"] +
                                (["symmetric_shift"] if causal else ["shift"]) + ["atomic_nondet"]) if s != headline]
     flops = counted_flops(B, H, S, D, causal)
+    tile_opts = {k: v for k, v in (("block_q", args.block_q), ("block_kv", args.block_kv)) if v}
     results = {}
     for sched in scheds:
         log(f"[bench] timing {sched}: warmup {args.warmup}, steps {args.steps}")
         opts = {"dq_mode": args.dq_mode} if (args.dq_mode != "default" and sched != "atomic_nondet") else {}
+        opts.update(tile_opts)
+        if args.ring_size and sched in ("shift", "symmetric_shift"):
+            opts["ring_size"] = args.ring_size
         r = time_schedule(da, torch, ev, tensors, (B, H, S, D), causal, sched, args.steps, args.warmup, **opts)
         r["tflops"] = flops / (r["ms_per_step"] * 1e-3) / 1e12
         results[sched] = r
         log(f"[bench] {sched}: {r['ms_per_step']:.3f} ms/step, main {r['main_ms']:.3f} ms, "
             f"{r['tflops']:.1f} TFLOP/s, status {r['status']}, repeat bitwise {r['repeat_bitwise']}")
     head = results[headline]
-    plan = da.detattn_bwd_plan(B, H, S, D, causal, headline)
+    plan_opts = dict(tile_opts)
+    if args.ring_size:
+        plan_opts["ring_size"] = args.ring_size
+    plan = da.detattn_bwd_plan(B, H, S, D, causal, headline, **plan_opts)
     tiles = tiles_executed(plan, B, H, causal)
     algo_flops = 10.0 * plan["block_q"] * plan["block_kv"] * D * tiles
     achieved = algo_flops / (head["main_ms"] * 1e-3) / 1e12
     atomic = results.get("atomic_nondet")
-    traffic = profiled_traffic(args.config)
+    traffic = profiled_traffic(args.config) if not plan_opts else None  # the record is for the default plan
     line = {
         "metric": "deterministic attn-bwd TFLOP/s (bf16, full+causal) and ratio vs atomic nondet",
         "value": round(head["tflops"], 2),
@@ -238,7 +249,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{'causal' if causal else 'full'} attention backward B={B} H={H} S={S} D={D}",
                    "schedule": headline, "block_q": plan["block_q"], "block_kv": plan["block_kv"],
-                   "grid": plan["grid"], "parallelism": "single GPU"},
+                   "grid": plan["grid"], "ring": plan["ring"], "parallelism": "single GPU"},
         "ratio_vs_atomic": round(head["tflops"] / atomic["tflops"], 4) if atomic else None,
         "schedules": {s: {"tflops": round(r["tflops"], 2), "ms_per_step": round(r["ms_per_step"], 4),
                           "main_ms": round(r["main_ms"], 4), "repeat_bitwise": r["repeat_bitwise"],

@@ -14,7 +14,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdetattn.so")
 
 MASKS = {"full": 0, "causal": 1}
-SCHEDULES = {"serial_ascending": 0, "descending_q": 1, "shift": 2, "symmetric_shift": 3, "atomic_nondet": 4}
+SCHEDULES = {"serial_ascending": 0, "descending_q": 1, "shift": 2, "symmetric_shift": 3, "atomic_nondet": 4,
+             "auto": 5}
+SCHEDULE_NAMES = {v: k for k, v in SCHEDULES.items()}
 DQ_MODES = {"default": 0, "rmw": 1, "atomic": 2, "xcd_local": 3}
 STATUS = {0: "OK", 1: "ERR_INVALID_ARG", 2: "ERR_UNSUPPORTED", 3: "ERR_WORKSPACE", 4: "ERR_HIP",
           5: "ERR_DEVICE_TIMEOUT", 6: "ERR_DEVICE_PLACEMENT"}
@@ -41,7 +43,7 @@ class BwdOptions(ctypes.Structure):
 
 class Plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("block_q", "block_kv", "n_q", "n_kv", "items", "grid", "ring", "rings",
-                                              "dq_mode", "cooperative")]
+                                              "dq_mode", "cooperative", "schedule")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

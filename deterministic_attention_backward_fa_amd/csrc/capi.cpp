@@ -25,7 +25,11 @@ bool shape_ok(const detattn_shape_t& s) {
 bool is_empty(const detattn_shape_t& s) { return s.B == 0 || s.H == 0 || s.S == 0; }
 
 // Library tile choice per head dimension and length: the KV tile (BKV rows,
-// owned by one workgroup) and the Q tile (BQ rows, one sweep step).
+// owned by one workgroup) and the Q tile (BQ rows, one sweep step), the
+// fastest measured on MI355X. At D = 128 the 128-row KV tile wins at every
+// length, 16k included, where the pages advise a smaller one for H800's
+// registers (explainer section 5.3): gfx950 keeps K, V and dK, dV of a
+// 128-row tile in its 512 registers per lane.
 void default_tiles(int D, int S, int& bq, int& bkv) {
   if (D == 64) {
     if (S % 128 == 0 && S >= 512) {
@@ -36,13 +40,8 @@ void default_tiles(int D, int S, int& bq, int& bkv) {
       bkv = 64;
     }
   } else {
-    if (S >= 16384 || S % 128 != 0) {
-      bq = 64;
-      bkv = 64;
-    } else {
-      bq = 64;
-      bkv = 128;
-    }
+    bq = 64;
+    bkv = S % 128 == 0 ? 128 : 64;
   }
 }
 
@@ -84,7 +83,7 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
               Plan& P) {
   if (!shape_ok(s) || is_empty(s)) return DETATTN_ERR_INVALID_ARG;
   if (mask != DETATTN_MASK_FULL && mask != DETATTN_MASK_CAUSAL) return DETATTN_ERR_INVALID_ARG;
-  if ((int)sch < 0 || (int)sch > 4) return DETATTN_ERR_INVALID_ARG;
+  if ((int)sch < 0 || (int)sch > 5) return DETATTN_ERR_INVALID_ARG;
   if (s.D != 64 && s.D != 128) return DETATTN_ERR_UNSUPPORTED;
   detattn_bwd_options_t o;
   std::memset(&o, 0, sizeof(o));
@@ -100,6 +99,8 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
   if (s.S % bq != 0 || s.S % bkv != 0) return DETATTN_ERR_UNSUPPORTED;
   const int causal = mask == DETATTN_MASK_CAUSAL;
   const int n_q = s.S / bq, n_kv = s.S / bkv, r = bkv / bq;
+  if (sch == DETATTN_AUTO)
+    sch = !causal ? DETATTN_SHIFT : n_kv % 2 == 0 ? DETATTN_SYMMETRIC_SHIFT : DETATTN_DESCENDING_Q;
   if (sch == DETATTN_SHIFT && causal) return DETATTN_ERR_UNSUPPORTED;
   if (sch == DETATTN_SYMMETRIC_SHIFT && (!causal || n_kv % 2 != 0)) return DETATTN_ERR_UNSUPPORTED;
 
@@ -174,6 +175,7 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
   P.pub.rings = rings;
   P.pub.dq_mode = pub_dqm;
   P.pub.cooperative = ring_sched ? 1 : 0;
+  P.pub.schedule = (int32_t)sch;
   P.causal = causal;
   P.sch = (int)sch;
   P.sc = sc;
@@ -224,7 +226,7 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
                               detattn_schedule_t schedule, const detattn_bwd_options_t* options, void* stream) {
   if (!shape_ok(s)) return DETATTN_ERR_INVALID_ARG;
   if (mask != DETATTN_MASK_FULL && mask != DETATTN_MASK_CAUSAL) return DETATTN_ERR_INVALID_ARG;
-  if ((int)schedule < 0 || (int)schedule > 4) return DETATTN_ERR_INVALID_ARG;
+  if ((int)schedule < 0 || (int)schedule > 5) return DETATTN_ERR_INVALID_ARG;
   if (is_empty(s)) return DETATTN_OK;
   const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
   for (const void* p : ptrs)

@@ -64,13 +64,20 @@ typedef enum { DETATTN_MASK_FULL = 0, DETATTN_MASK_CAUSAL = 1 } detattn_mask_t;
  *  ATOMIC_NONDET     unordered fp32 atomic adds of the dQ partials: the
  *                    non-deterministic speed reference (explainer 2.1;
  *                    summary 1). dK and dV remain deterministic.
+ *  AUTO              the deterministic schedule measured fastest on MI355X
+ *                    for the mask (the pages' future "dynamic scheduling",
+ *                    explainer section 7): SHIFT for full masks,
+ *                    SYMMETRIC_SHIFT for causal masks with an even number of
+ *                    KV tiles, else DESCENDING_Q. The choice depends on the
+ *                    shape only; detattn_plan_t.schedule reports it.
  */
 typedef enum {
   DETATTN_SERIAL_ASCENDING = 0,
   DETATTN_DESCENDING_Q = 1,
   DETATTN_SHIFT = 2,
   DETATTN_SYMMETRIC_SHIFT = 3,
-  DETATTN_ATOMIC_NONDET = 4
+  DETATTN_ATOMIC_NONDET = 4,
+  DETATTN_AUTO = 5
 } detattn_schedule_t;
 
 typedef enum {
@@ -144,6 +151,7 @@ typedef struct {
   int32_t rings;       /* rings running at once, else 0 */
   int32_t dq_mode;     /* resolved detattn_dq_mode_t (0 for ATOMIC_NONDET) */
   int32_t cooperative; /* 1 if launched as a cooperative (co-resident) grid */
+  int32_t schedule;    /* the schedule that runs (AUTO resolved) */
 } detattn_plan_t;
 
 /*

@@ -112,8 +112,8 @@ def test_fwd_argument_errors():
     (4, 16, 2048, 64, True, "symmetric_shift", 128, 128),
     (2, 32, 4096, 128, False, "shift", 64, 128),
     (1, 32, 8192, 128, True, "symmetric_shift", 64, 128),
-    (1, 16, 16384, 128, False, "shift", 64, 64),
-    (1, 16, 16384, 128, True, "symmetric_shift", 64, 64),
+    (1, 16, 16384, 128, False, "shift", 64, 128),           # 128-row KV tiles at 16k too (measured faster)
+    (1, 16, 16384, 128, True, "symmetric_shift", 64, 128),
 ])
 def test_default_tiles_and_rings(cfg):
     B, H, S, D, causal, sched, bq, bkv = cfg
@@ -189,13 +189,28 @@ def test_library_ring_ranks_match_oracle(sched, mask, n_kv, r):
 def test_ring_option_in_plan():
     """Default rings: a head's items if they fit one XCD (32 workgroups), else
     the largest divisor <= 32; an explicit ring_size must divide the items."""
-    p = da.detattn_bwd_plan(1, 16, 16384, 128, True, "symmetric_shift", grid=256)
+    kv64 = dict(block_q=64, block_kv=64)
+    p = da.detattn_bwd_plan(1, 16, 16384, 128, True, "symmetric_shift", grid=256, **kv64)
     assert (p["n_kv"], p["ring"], p["rings"], p["grid"]) == (256, 32, 8, 256)
-    p = da.detattn_bwd_plan(1, 16, 16384, 128, False, "shift", grid=256)
-    assert (p["ring"], p["rings"]) == (32, 8)
+    p = da.detattn_bwd_plan(1, 16, 16384, 128, False, "shift", grid=256, **kv64)
+    assert (p["ring"], p["rings"], p["dq_mode"]) == (32, 8, da.DQ_MODES["xcd_local"])
+    p = da.detattn_bwd_plan(1, 16, 16384, 128, True, "symmetric_shift", grid=256)
+    assert (p["n_kv"], p["ring"], p["rings"]) == (128, 32, 8)
     p = da.detattn_bwd_plan(1, 32, 8192, 128, True, "symmetric_shift", grid=256)
     assert (p["ring"], p["rings"]) == (32, 8)
-    p = da.detattn_bwd_plan(1, 16, 16384, 128, False, "shift", grid=256, ring_size=256)
+    p = da.detattn_bwd_plan(1, 16, 16384, 128, False, "shift", grid=256, ring_size=256, **kv64)
     assert (p["ring"], p["rings"], p["dq_mode"]) == (256, 1, da.DQ_MODES["atomic"])
     with pytest.raises(da.DetAttnError):
-        da.detattn_bwd_plan(1, 16, 16384, 128, False, "shift", grid=256, ring_size=48)
+        da.detattn_bwd_plan(1, 16, 16384, 128, False, "shift", grid=256, ring_size=48, **kv64)
+
+
+@pytest.mark.parametrize("S,D,causal,want", [
+    (4096, 128, False, "shift"), (8192, 128, True, "symmetric_shift"), (2048, 64, True, "symmetric_shift"),
+    (16384, 128, False, "shift"), (384, 128, True, "descending_q"),   # 3 KV tiles: no symmetric pairing
+    (192, 128, True, "descending_q"),                                  # 64-row KV tiles (S % 128 != 0), 3 of them
+])
+def test_auto_schedule_resolves_from_the_shape(S, D, causal, want):
+    p = da.detattn_bwd_plan(1, 2, S, D, causal, "auto", grid=256)
+    assert da.SCHEDULE_NAMES[p["schedule"]] == want
+    q = da.detattn_bwd_plan(1, 2, S, D, causal, want, grid=256)
+    assert p == q

@@ -24,12 +24,15 @@ from gpu_util import TOL, rel_err, same_bits, say
 pytestmark = pytest.mark.gpu
 
 CONFIGS = {
-    # name: (B, H, S, D, causal, seed, runs for the determinism check)
-    "causal_b4_h16_s2048_d64": (4, 16, 2048, 64, True, 102, 3),
-    "full_b2_h32_s4096_d128": (2, 32, 4096, 128, False, 103, 3),
-    "causal_b1_h32_s8192_d128": (1, 32, 8192, 128, True, 104, 3),
-    "full_b1_h16_s16384_d128": (1, 16, 16384, 128, False, 105, 100),
-    "causal_b1_h16_s16384_d128": (1, 16, 16384, 128, True, 105, 100),
+    # name: (B, H, S, D, causal, seed, runs for the determinism check, options)
+    "causal_b4_h16_s2048_d64": (4, 16, 2048, 64, True, 102, 3, {}),
+    "full_b2_h32_s4096_d128": (2, 32, 4096, 128, False, 103, 3, {}),
+    "causal_b1_h32_s8192_d128": (1, 32, 8192, 128, True, 104, 3, {}),
+    # the long-context workload with its stated 64-row KV tile, then with the library's default tile
+    "full_b1_h16_s16384_d128_kv64": (1, 16, 16384, 128, False, 105, 100, {"block_q": 64, "block_kv": 64}),
+    "causal_b1_h16_s16384_d128_kv64": (1, 16, 16384, 128, True, 105, 100, {"block_q": 64, "block_kv": 64}),
+    "full_b1_h16_s16384_d128": (1, 16, 16384, 128, False, 105, 100, {}),
+    "causal_b1_h16_s16384_d128": (1, 16, 16384, 128, True, 105, 100, {}),
 }
 
 
@@ -39,7 +42,7 @@ def schedules_for(causal):
 
 @pytest.mark.parametrize("name", list(CONFIGS))
 def test_fullsize_sampled_parity_and_determinism(name):
-    B, H, S, D, causal, seed, runs = CONFIGS[name]
+    B, H, S, D, causal, seed, runs, opts = CONFIGS[name]
     scale = 1.0 / math.sqrt(D)
     say(f"[fullsize] {name}: inputs")
     cpu = make_qkvdo(B, H, S, D, seed)
@@ -58,10 +61,10 @@ def test_fullsize_sampled_parity_and_determinism(name):
         assert np.max(np.abs(lse[b, h].cpu().numpy() - refs[(b, h)][3])) <= 1e-3
     outs = {}
     for sched in schedules_for(causal):
-        say(f"[fullsize] {name}: {sched} plan {da.detattn_bwd_plan(B, H, S, D, causal, sched)}")
+        say(f"[fullsize] {name}: {sched} plan {da.detattn_bwd_plan(B, H, S, D, causal, sched, **opts)}")
         ws = da.alloc_workspace(B, H, S, D)
         first = [t.clone() for t in da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule=sched,
-                                                             workspace=ws)]
+                                                             workspace=ws, **opts)]
         assert da.detattn_device_status(ws) == 0
         for (b, h) in heads:
             rdq, rdk, rdv, _, _ = refs[(b, h)]
@@ -72,11 +75,18 @@ def test_fullsize_sampled_parity_and_determinism(name):
         if sched != "atomic_nondet":
             out = tuple(torch.empty_like(t) for t in first)
             for _ in range(runs - 1):
-                da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule=sched, workspace=ws, out=out)
+                da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule=sched, workspace=ws, out=out,
+                                          **opts)
                 for a, b_ in zip(first, out):
                     assert same_bits(a, b_), f"{name} {sched} not bit-identical across runs"
             assert da.detattn_device_status(ws) == 0
         outs[sched] = first
+    if not opts:
+        # the automatic choice is the measured-fastest deterministic schedule: same plan, same bits
+        auto = da.detattn_bwd_plan(B, H, S, D, causal, "auto")
+        name_auto = da.SCHEDULE_NAMES[auto["schedule"]]
+        got = da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule="auto")
+        assert all(same_bits(a, b_) for a, b_ in zip(outs[name_auto], got)), name_auto
     assert same_bits(outs["serial_ascending"][0], outs["descending_q"][0])
     assert same_bits(outs["serial_ascending"][1], outs["atomic_nondet"][1])
     assert same_bits(outs["serial_ascending"][2], outs["atomic_nondet"][2])
