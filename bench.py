@@ -166,6 +166,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="causal_b1_h32_s8192_d128", choices=sorted(CONFIGS))
+    ap.add_argument("--shape", default=None,
+                    help="another workload instead of --config: B,H,S,D,full|causal (inputs seeded with 200)")
     ap.add_argument("--schedule", default=None, help="headline schedule (default: shift / symmetric_shift)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-headline", action="store_true", help="skip the other schedules")
@@ -198,7 +200,14 @@ def main():
     import deterministic_attention_backward_fa_amd as da
     from deterministic_attention_backward_fa_amd.synth import make_qkvdo
 
-    B, H, S, D, causal, seed = CONFIGS[args.config]
+    if args.shape:
+        f = args.shape.split(",")
+        if len(f) != 5 or f[4] not in ("full", "causal"):
+            ap.error("--shape takes B,H,S,D,full|causal")
+        B, H, S, D, causal, seed = int(f[0]), int(f[1]), int(f[2]), int(f[3]), f[4] == "causal", 200
+        args.config = f"{f[4]}_b{B}_h{H}_s{S}_d{D}"
+    else:
+        B, H, S, D, causal, seed = CONFIGS[args.config]
     headline = args.schedule or ("symmetric_shift" if causal else "shift")
     log(f"[bench] {args.config}: generating inputs (seed {seed})")
     q, k, v, do = (t.cuda() for t in make_qkvdo(B, H, S, D, seed))
