@@ -18,6 +18,7 @@ SCHEDULES = {"serial_ascending": 0, "descending_q": 1, "shift": 2, "symmetric_sh
              "auto": 5}
 SCHEDULE_NAMES = {v: k for k, v in SCHEDULES.items()}
 DQ_MODES = {"default": 0, "rmw": 1, "atomic": 2, "xcd_local": 3}
+DISPATCH = {"default": 0, "ticket": 1, "ring": 2}
 STATUS = {0: "OK", 1: "ERR_INVALID_ARG", 2: "ERR_UNSUPPORTED", 3: "ERR_WORKSPACE", 4: "ERR_HIP",
           5: "ERR_DEVICE_TIMEOUT", 6: "ERR_DEVICE_PLACEMENT"}
 
@@ -38,7 +39,8 @@ class BwdOptions(ctypes.Structure):
                 ("xcd_remap", ctypes.c_int32), ("dq_mode", ctypes.c_int32), ("debug_delay_seed", ctypes.c_uint32),
                 ("timeout_us", ctypes.c_uint32), ("debug_skip_signal", ctypes.c_int32),
                 ("main_begin_event", ctypes.c_void_p), ("main_end_event", ctypes.c_void_p),
-                ("trace", ctypes.c_void_p), ("trace_records", ctypes.c_int32), ("ring_size", ctypes.c_int32)]
+                ("trace", ctypes.c_void_p), ("trace_records", ctypes.c_int32), ("ring_size", ctypes.c_int32),
+                ("dispatch", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -125,11 +127,12 @@ def _check_tensor(name, t, dtype, shape):
 
 def _options(block_q=0, block_kv=0, grid=0, xcd_remap=None, dq_mode="default", debug_delay_seed=0, timeout_us=0,
              debug_skip_signal=0, main_begin_event=None, main_end_event=None, trace=None, trace_records=0,
-             ring_size=0):
+             ring_size=0, dispatch="default"):
     xr = 0 if xcd_remap is None else (1 if xcd_remap else 2)
     return BwdOptions(int(block_q), int(block_kv), int(grid), xr, DQ_MODES[dq_mode], int(debug_delay_seed),
                       int(timeout_us), int(debug_skip_signal), main_begin_event, main_end_event,
-                      trace.data_ptr() if trace is not None else None, int(trace_records), int(ring_size))
+                      trace.data_ptr() if trace is not None else None, int(trace_records), int(ring_size),
+                      DISPATCH[dispatch])
 
 
 def detattn_fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
@@ -169,7 +172,7 @@ def alloc_workspace(B, H, S, D, device="cuda"):
 def attn_bwd_deterministic(q, k, v, o, dout, lse, causal=False, schedule="serial_ascending", scale=None,
                            workspace=None, out=None, stream=None, **opts):
     """dQ, dK, dV (bf16) of softmax attention. `opts` are BwdOptions fields
-    (block_q, block_kv, grid, xcd_remap, dq_mode, debug_delay_seed, timeout_us, debug_skip_signal, ring_size)."""
+    (block_q, block_kv, grid, xcd_remap, dq_mode, debug_delay_seed, timeout_us, debug_skip_signal, ring_size, dispatch)."""
     B, H, S, D = q.shape
     for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
         _check_tensor(n, t, torch.bfloat16, (B, H, S, D))

@@ -89,7 +89,7 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
   std::memset(&o, 0, sizeof(o));
   if (opt) o = *opt;
   if (o.block_q < 0 || o.block_kv < 0 || o.grid < 0 || o.xcd_remap < 0 || o.xcd_remap > 2 || o.dq_mode < 0 ||
-      o.dq_mode > 3 || o.ring_size < 0)
+      o.dq_mode > 3 || o.ring_size < 0 || o.dispatch < 0 || o.dispatch > 2)
     return DETATTN_ERR_INVALID_ARG;
   int bq, bkv;
   default_tiles(s.D, s.S, bq, bkv);
@@ -109,13 +109,9 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
   const MainInfo info0 = main_info(s.D, bq, bkv, causal, kDqOrderedRmw, false);
   if (!info0.func) return DETATTN_ERR_UNSUPPORTED;
 
-  const bool ring_sched = (sch == DETATTN_SHIFT || sch == DETATTN_SYMMETRIC_SHIFT);
   Sched sc{(int)sch, causal, n_q, n_kv, r, 0};
-  if (ring_sched) {
-    const int ip = sc.items_per_head();
-    sc.G = o.ring_size ? o.ring_size : default_ring(ip);
-    if (ip % sc.G != 0) return DETATTN_ERR_UNSUPPORTED;
-  }
+  const int ip = sc.items_per_head();
+  const int ring_pref = o.ring_size ? o.ring_size : default_ring(ip);
   const long long BH = (long long)s.B * s.H;
   const long long items = BH * sc.items_per_head();
   int capacity = 0;  // co-resident workgroups
@@ -128,6 +124,18 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
   int grid = o.grid ? o.grid : capacity;
   int ring = 0, rings = 0;
   int xcd = o.xcd_remap != 2;
+  // Shift schedules always run on rings. Serial and descending run on rings too
+  // where a ring fits one XCD (their ordered adds then stay in that XCD's L2),
+  // else on the ticket counter; their order (rank = KV tile) is the same.
+  bool ring_sched = sch == DETATTN_SHIFT || sch == DETATTN_SYMMETRIC_SHIFT;
+  if (sch == DETATTN_SERIAL_ASCENDING || sch == DETATTN_DESCENDING_Q) {
+    if (o.dispatch == 2) ring_sched = true;
+    else if (o.dispatch == 0) ring_sched = xcd && grid % 8 == 0 && ring_pref <= grid / 8 && ip % ring_pref == 0;
+  }
+  if (ring_sched) {
+    sc.G = ring_pref;
+    if (ip % sc.G != 0) return DETATTN_ERR_UNSUPPORTED;
+  }
   if (ring_sched) {
     // Every ring (G workgroups sharing one head's items) must be co-resident.
     // With the XCD remap a ring occupies consecutive slots of one XCD

@@ -128,6 +128,12 @@ typedef struct {
                                 (the pages' schedules are the single round G = items per head). G sets the
                                 accumulation order: results are bit-identical across calls with the same G.
                                 Invalid (UNSUPPORTED) if it does not divide the item count. */
+  int32_t dispatch;          /* SERIAL_ASCENDING / DESCENDING_Q: 1 = ticket counter in (head, KV tile) order,
+                                2 = static rings like the shift schedules (ring_size applies; a ring of one
+                                XCD keeps the ordered dQ adds in that XCD's L2), 0 = default: rings where a
+                                ring fits one XCD, else the ticket counter. The accumulation order, rank =
+                                KV tile, is the same in both. Ignored by the other schedules (rings for
+                                SHIFT / SYMMETRIC_SHIFT, ticket for ATOMIC_NONDET). */
 } detattn_bwd_options_t;
 
 /* Phase ids written into the optional trace (low 8 bits of the second word). */

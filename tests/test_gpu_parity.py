@@ -35,6 +35,10 @@ SMALL = [
 ]
 
 
+def plan_mode_name(plan):
+    return {v: k for k, v in da.DQ_MODES.items()}[plan["dq_mode"]]
+
+
 def schedules_for(causal):
     base = ["serial_ascending", "descending_q", "atomic_nondet"]
     return base + (["symmetric_shift"] if causal else ["shift"])
@@ -110,6 +114,11 @@ def test_invariance_grid_placement_delays(case):
         plan = da.detattn_bwd_plan(B, H, S, D, causal, sched, **opts)
         variants = [dict(debug_delay_seed=12345), dict(xcd_remap=False), dict(dq_mode="atomic"),
                     dict(dq_mode="rmw")]
+        if sched in ("serial_ascending", "descending_q"):
+            # static rings instead of the ticket counter: the same order (rank = KV tile), so the
+            # same add mechanism gives the same bits
+            variants += [dict(dispatch="ring"), dict(dispatch="ring", dq_mode=plan_mode_name(plan)),
+                         dict(dispatch="ring", ring_size=1, grid=8)]
         ring = plan["ring"]
         if ring:
             variants.append(dict(grid=ring))           # a single ring at a time
@@ -131,18 +140,20 @@ def test_invariance_grid_placement_delays(case):
                 assert rel_err(got[0].float().cpu().numpy(), base[0].float().cpu().numpy()) <= 1e-2
 
 
-def test_timeout_path_reports_and_exits():
+@pytest.mark.parametrize("dispatch", ["ticket", "ring"])
+def test_timeout_path_reports_and_exits(dispatch):
     """Withhold one workgroup's first dQ signal: its successor's bounded wait
     expires, the error word is set and every kernel still exits."""
     B, H, S, D = 1, 1, 256, 64
     _, (q, k, v, do, o, lse) = inputs(B, H, S, D, 3, False)
     ws = da.alloc_workspace(B, H, S, D)
-    say("[timeout path] serial_ascending, item 0 withholds its first signal")
+    say(f"[timeout path] serial_ascending ({dispatch} dispatch), item 0 withholds its first signal")
     da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=False, schedule="serial_ascending", workspace=ws,
-                              debug_skip_signal=1, timeout_us=2000)
+                              debug_skip_signal=1, timeout_us=2000, dispatch=dispatch)
     assert da.detattn_device_status(ws) == 5
     # the next normal call on the same workspace is clean again
-    da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=False, schedule="serial_ascending", workspace=ws)
+    da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=False, schedule="serial_ascending", workspace=ws,
+                              dispatch=dispatch)
     assert da.detattn_device_status(ws) == 0
 
 
