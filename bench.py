@@ -176,7 +176,7 @@ def main():
     ap.add_argument("--block-q", type=int, default=0, help="Q tile rows (0 = library default)")
     ap.add_argument("--block-kv", type=int, default=0, help="KV tile rows (0 = library default)")
     ap.add_argument("--dispatch", default="default", choices=["default", "ticket", "ring"],
-                    help="serial_ascending / descending_q: ticket counter or static rings")
+                    help="serial_ascending / descending_q / atomic_nondet: ticket counter or static rings")
     ap.add_argument("--ring-size", type=int, default=0,
                     help="workgroups per ring of the shift schedules (0 = library default)")
     ap.add_argument("--trace", action="store_true", help="log the headline schedule's per-tile phase breakdown")
@@ -230,7 +230,7 @@ def main():
         opts.update(tile_opts)
         if args.ring_size and sched in ("shift", "symmetric_shift"):
             opts["ring_size"] = args.ring_size
-        if args.dispatch != "default" and sched in ("serial_ascending", "descending_q"):
+        if args.dispatch != "default" and sched in ("serial_ascending", "descending_q", "atomic_nondet"):
             opts["dispatch"] = args.dispatch
         r = time_schedule(da, torch, ev, tensors, (B, H, S, D), causal, sched, args.steps, args.warmup, **opts)
         r["tflops"] = flops / (r["ms_per_step"] * 1e-3) / 1e12

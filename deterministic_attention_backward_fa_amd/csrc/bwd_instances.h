@@ -31,6 +31,7 @@ MainInfo pick_mode(int dqm) {
     case kDqOrderedAtomic: return info_of<D, BQ, BKV, CAUSAL, kDqOrderedAtomic, TRACE>();
     case kDqUnordered: return info_of<D, BQ, BKV, CAUSAL, kDqUnordered, TRACE>();
     case kDqLocalRmw: return info_of<D, BQ, BKV, CAUSAL, kDqLocalRmw, TRACE>();
+    case kDqUnorderedLocal: return info_of<D, BQ, BKV, CAUSAL, kDqUnorderedLocal, TRACE>();
     default: return MainInfo{nullptr, 0, 0};
   }
 }

@@ -25,7 +25,13 @@ namespace detattn {
 // kDqLocalRmw: ordered read-modify-write whose accumulator and flag accesses
 // use sc0 (L2-coherent) instead of sc1 (coherent across XCDs); valid only when
 // every workgroup touching a head's dQ tiles runs on one XCD.
-enum DqMode : int { kDqOrderedRmw = 1, kDqOrderedAtomic = 2, kDqUnordered = 3, kDqLocalRmw = 4 };
+enum DqMode : int {
+  kDqOrderedRmw = 1,       // ordered read-modify-write, device scope
+  kDqOrderedAtomic = 2,    // ordered fp32 atomic adds, device scope
+  kDqUnordered = 3,        // unordered fp32 atomic adds, device scope (non-deterministic)
+  kDqLocalRmw = 4,         // ordered read-modify-write in one XCD's L2
+  kDqUnorderedLocal = 5    // unordered fp32 atomic adds in one XCD's L2 (non-deterministic)
+};
 
 struct BwdArgs {
   const __bf16* q;

@@ -497,7 +497,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   // L2 (sc0) when every workgroup of a ring runs on one XCD. sc0 loads may hit
   // the compute unit's own L1, so that mode invalidates L1 (buffer_inv sc0)
   // after observing the flag and before loading. Flags always use sc1.
-  constexpr int kScope = DQM == kDqLocalRmw ? __HIP_MEMORY_SCOPE_WORKGROUP : __HIP_MEMORY_SCOPE_AGENT;
+  constexpr bool kLocal = DQM == kDqLocalRmw || DQM == kDqUnorderedLocal;
+  constexpr bool kUnordered = DQM == kDqUnordered || DQM == kDqUnorderedLocal;
+  constexpr int kScope = kLocal ? __HIP_MEMORY_SCOPE_WORKGROUP : __HIP_MEMORY_SCOPE_AGENT;
   constexpr int kFlagScope = __HIP_MEMORY_SCOPE_AGENT;
   constexpr bool kRmw = DQM == kDqOrderedRmw || DQM == kDqLocalRmw;
   constexpr int kWaves = kThreads / 64;
@@ -568,7 +570,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       slot = wg % a.ring;
     }
     if (ring_id >= a.rings) return;
-    if constexpr (DQM == kDqLocalRmw) {
+    if constexpr (kLocal) {
       // the ring placement assumes workgroup w runs on XCD w % 8: verify it
       unsigned xcc;
       asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
@@ -760,7 +762,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
         }
       };
       // this tile's turn in dQ tile i's order: rank rk; the flag counts the wave contributions added
-      const int rk = DQM == kDqUnordered ? 0 : cur.rank_now();
+      const int rk = kUnordered ? 0 : cur.rank_now();
       int* flag = a.flags + ((long long)bh * sc.n_q + i) * kFlagInts;
       int seen = rk;  // the flag as last read (read in stream A)
       const int vb = C::OFF_B0 + b * C::BUF;
@@ -871,7 +873,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       });
       static_for<0, SA::N>([&](auto kc) {
         constexpr int k = decltype(kc)::value;
-        if constexpr (DQM != kDqUnordered && k == SA::kPub) {
+        if constexpr (!kUnordered && k == SA::kPub) {
           // publish the previous tile's contribution once its writes have
           // landed: only this tile's DMA was issued after them, and vector
           // memory operations complete in issue order
@@ -881,7 +883,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
             pend = nullptr;
           }
         }
-        if constexpr (DQM != kDqUnordered && k == SA::kFlag) {
+        if constexpr (!kUnordered && k == SA::kFlag) {
           // the dQ tile's flag, read late in stream A (every lane reads the
           // same word; also by the first contributor, so this read is always
           // the wave's newest vector-memory operation at the barrier); it is
@@ -917,7 +919,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       // this wave's share of the next tile (DMA issued early in stream A) has
       // landed: after the barrier below the whole next tile is in LDS. The
       // flag read, issued after it, may stay in flight.
-      vm_wait<DQM != kDqUnordered ? 1 : 0>();
+      vm_wait<!kUnordered ? 1 : 0>();
 
       // The turn has come once every wave of every earlier contributor has
       // added: flag >= kWaves * rk. The counter only grows, and a wave of this
@@ -1052,13 +1054,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       // after the dQ MFMAs: wait for the turn if it had not come (RMW: then read
       // the accumulator), or issue the adds themselves (atomic modes)
       auto adds_begin = [&]() {
-        if constexpr (DQM == kDqUnordered) {
+        if constexpr (kUnordered) {
+          // device scope, or (local mode: every add to a dQ tile comes from one XCD) in that XCD's L2
 #pragma unroll
           for (int m = 0; m < NQB; ++m)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-              __hip_atomic_fetch_add(dqp(m, r), dqAcc[m][r], __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
+              __hip_atomic_fetch_add(dqp(m, r), dqAcc[m][r], __ATOMIC_RELAXED, kScope);
         } else {
           if (!early) {
             turn();
@@ -1089,7 +1091,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       static_for<0, PF>([&](auto lc) { loadB(lc, ring[decltype(lc)::value]); });
       static_for<0, NB>([&](auto kc) {
         constexpr int k = decltype(kc)::value;
-        if constexpr (k == kDecide && DQM != kDqUnordered) {
+        if constexpr (k == kDecide && !kUnordered) {
           early = rk == 0 || (a.delay_seed == 0 && __builtin_amdgcn_readfirstlane(seen) >= turn_val);
           // early: the turn has come, the accumulator is read under the dQ MFMAs
           // (local mode drops stale L1 lines first); otherwise it is read after
@@ -1154,7 +1156,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       // landed: early in the next tile's stream A, or at the end of the column.
       // The flag counts wave contributions, so no barrier sits between the
       // adds and the hand-off to the next contributor.
-      if constexpr (DQM != kDqUnordered) {
+      if constexpr (!kUnordered) {
         const bool withhold = (a.skip_item >= 0 && gidx == a.skip_item && t == 0);
         pend = withhold ? nullptr : flag;
       }

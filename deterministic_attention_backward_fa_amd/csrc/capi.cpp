@@ -124,13 +124,16 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
   int grid = o.grid ? o.grid : capacity;
   int ring = 0, rings = 0;
   int xcd = o.xcd_remap != 2;
-  // Shift schedules always run on rings. Serial and descending run on rings too
-  // where a ring fits one XCD (their ordered adds then stay in that XCD's L2),
-  // else on the ticket counter; their order (rank = KV tile) is the same.
+  // Shift schedules always run on rings. Serial and descending run on rings
+  // too where a ring fits one XCD (their ordered adds then stay in that XCD's
+  // L2), else on the ticket counter; the order (rank = KV tile) is the same.
+  // The atomic reference stays on the ticket counter with device-scope adds
+  // unless asked: its adds confined to one XCD's L2 measured slower.
   bool ring_sched = sch == DETATTN_SHIFT || sch == DETATTN_SYMMETRIC_SHIFT;
-  if (sch == DETATTN_SERIAL_ASCENDING || sch == DETATTN_DESCENDING_Q) {
+  if (sch == DETATTN_SERIAL_ASCENDING || sch == DETATTN_DESCENDING_Q || sch == DETATTN_ATOMIC_NONDET) {
     if (o.dispatch == 2) ring_sched = true;
-    else if (o.dispatch == 0) ring_sched = xcd && grid % 8 == 0 && ring_pref <= grid / 8 && ip % ring_pref == 0;
+    else if (o.dispatch == 0 && sch != DETATTN_ATOMIC_NONDET)
+      ring_sched = xcd && grid % 8 == 0 && ring_pref <= grid / 8 && ip % ring_pref == 0;
   }
   if (ring_sched) {
     sc.G = ring_pref;
@@ -160,8 +163,9 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
   }
 
   // dQ accumulation mode
-  int dqm = kDqUnordered;
-  int pub_dqm = 0;
+  // (ATOMIC_NONDET: unordered atomic adds, in one XCD's L2 when its rings sit on one XCD)
+  int dqm = ring_sched && xcd ? kDqUnorderedLocal : kDqUnordered;
+  int pub_dqm = dqm == kDqUnorderedLocal ? DETATTN_DQ_XCD_LOCAL_RMW : 0;
   if (sch != DETATTN_ATOMIC_NONDET) {
     const bool local_ok = ring_sched && xcd;
     pub_dqm = o.dq_mode;
@@ -258,7 +262,7 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
   hipStream_t st_ = static_cast<hipStream_t>(stream);
   const long long rows = BH * s.S;
   const long long elems = rows * s.D;
-  const bool unordered = P.dqm_internal == kDqUnordered;
+  const bool unordered = P.dqm_internal == kDqUnordered || P.dqm_internal == kDqUnorderedLocal;
 
   hipError_t e = launch_pre(s.D, static_cast<const __bf16*>(o), static_cast<const __bf16*>(dout), lse, 1.f / s.softmax_scale,
                             nlse, ndelta, rows, flags,

@@ -128,12 +128,15 @@ typedef struct {
                                 (the pages' schedules are the single round G = items per head). G sets the
                                 accumulation order: results are bit-identical across calls with the same G.
                                 Invalid (UNSUPPORTED) if it does not divide the item count. */
-  int32_t dispatch;          /* SERIAL_ASCENDING / DESCENDING_Q: 1 = ticket counter in (head, KV tile) order,
-                                2 = static rings like the shift schedules (ring_size applies; a ring of one
-                                XCD keeps the ordered dQ adds in that XCD's L2), 0 = default: rings where a
-                                ring fits one XCD, else the ticket counter. The accumulation order, rank =
-                                KV tile, is the same in both. Ignored by the other schedules (rings for
-                                SHIFT / SYMMETRIC_SHIFT, ticket for ATOMIC_NONDET). */
+  int32_t dispatch;          /* SERIAL_ASCENDING / DESCENDING_Q / ATOMIC_NONDET: 1 = ticket counter in (head,
+                                KV tile) order, 2 = static rings like the shift schedules (ring_size applies;
+                                a ring of one XCD keeps the dQ adds in that XCD's L2: read-modify-write for
+                                the ordered schedules, fp32 atomic adds for ATOMIC_NONDET), 0 = default:
+                                SERIAL_ASCENDING / DESCENDING_Q on rings where a ring fits one XCD, else
+                                on the ticket counter; ATOMIC_NONDET on the ticket counter with
+                                device-scope adds (measured faster than adds kept in one XCD's L2). The
+                                accumulation order of the ordered schedules, rank = KV tile, is the same
+                                in both. Ignored by SHIFT / SYMMETRIC_SHIFT (always rings). */
 } detattn_bwd_options_t;
 
 /* Phase ids written into the optional trace (low 8 bits of the second word). */
@@ -155,7 +158,8 @@ typedef struct {
   int32_t grid;        /* workgroups launched */
   int32_t ring;        /* workgroups per co-resident ring G (shift schedules), else 0 */
   int32_t rings;       /* rings running at once, else 0 */
-  int32_t dq_mode;     /* resolved detattn_dq_mode_t (0 for ATOMIC_NONDET) */
+  int32_t dq_mode;     /* resolved detattn_dq_mode_t; ATOMIC_NONDET: 0 = device-scope atomic adds,
+                          DETATTN_DQ_XCD_LOCAL_RMW = atomic adds in one XCD's L2 (rings of one XCD) */
   int32_t cooperative; /* 1 if launched as a cooperative (co-resident) grid */
   int32_t schedule;    /* the schedule that runs (AUTO resolved) */
 } detattn_plan_t;

@@ -130,18 +130,24 @@ def test_default_tiles_and_rings(cfg):
 def test_ticket_plan_caps_grid_at_items():
     p = da.detattn_bwd_plan(1, 2, 256, 64, False, "serial_ascending", grid=256, dispatch="ticket")
     assert p["items"] == 2 * 4 and p["grid"] == 8 and p["ring"] == 0 and p["cooperative"] == 0
-    p = da.detattn_bwd_plan(1, 2, 256, 64, False, "atomic_nondet", grid=256)
-    assert p["grid"] == 8 and p["ring"] == 0 and p["cooperative"] == 0
+    p = da.detattn_bwd_plan(1, 2, 256, 64, False, "atomic_nondet", grid=256, dispatch="ticket")
+    assert p["grid"] == 8 and p["ring"] == 0 and p["cooperative"] == 0 and p["dq_mode"] == 0
 
 
-@pytest.mark.parametrize("sched", ["serial_ascending", "descending_q"])
-def test_serial_and_descending_default_to_xcd_rings(sched):
+@pytest.mark.parametrize("sched", ["serial_ascending", "descending_q", "atomic_nondet"])
+def test_serial_descending_atomic_rings(sched):
     """Serial and descending run on rings of one XCD where one fits (their
-    ordered adds stay in that XCD's L2), else on the ticket counter."""
-    p = da.detattn_bwd_plan(1, 32, 8192, 128, True, sched, grid=256)
+    ordered adds stay in that XCD's L2), else on the ticket counter; the
+    atomic reference takes rings (adds in one XCD's L2) only when asked."""
+    ask = {"dispatch": "ring"} if sched == "atomic_nondet" else {}
+    p = da.detattn_bwd_plan(1, 32, 8192, 128, True, sched, grid=256, **ask)
     assert (p["ring"], p["rings"], p["cooperative"], p["dq_mode"]) == (32, 8, 1, da.DQ_MODES["xcd_local"])
+    if sched == "atomic_nondet":
+        p = da.detattn_bwd_plan(1, 32, 8192, 128, True, sched, grid=256)
+        assert (p["ring"], p["cooperative"], p["dq_mode"]) == (0, 0, 0)
     p = da.detattn_bwd_plan(1, 32, 8192, 128, True, sched, grid=100)       # no XCD placement: ticket
-    assert (p["ring"], p["cooperative"], p["dq_mode"]) == (0, 0, da.DQ_MODES["atomic"])
+    device_mode = 0 if sched == "atomic_nondet" else da.DQ_MODES["atomic"]
+    assert (p["ring"], p["cooperative"], p["dq_mode"]) == (0, 0, device_mode)
     p = da.detattn_bwd_plan(1, 32, 8192, 128, True, sched, grid=256, dispatch="ticket")
     assert (p["ring"], p["cooperative"]) == (0, 0)
     p = da.detattn_bwd_plan(1, 32, 8192, 128, True, sched, grid=256, dispatch="ring", ring_size=16)

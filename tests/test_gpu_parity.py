@@ -77,6 +77,17 @@ def test_backward_matches_oracle_all_schedules(case):
             e = rel_err(got.float().cpu().numpy(), want)
             assert e <= TOL, f"{sched} {name} rel err {e:.3e}"
         res[sched] = (dq, dk, dv)
+    # the atomic reference both ways: device-scope atomics (ticket counter, the
+    # default) and atomics in one XCD's L2 (rings of one XCD)
+    say(f"[bwd parity] {case} atomic_nondet ring dispatch")
+    ws = da.alloc_workspace(B, H, S, D)
+    dq, dk, dv = da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule="atomic_nondet",
+                                           workspace=ws, dispatch="ring", **opts)
+    assert da.detattn_device_status(ws) == 0
+    for name, got, want in (("dq", dq, dq_r), ("dk", dk, dk_r), ("dv", dv, dv_r)):
+        e = rel_err(got.float().cpu().numpy(), want)
+        assert e <= TOL, f"atomic_nondet (ring) {name} rel err {e:.3e}"
+    assert same_bits(res["atomic_nondet"][1], dk) and same_bits(res["atomic_nondet"][2], dv)
     # shared accumulation orders give identical bits
     assert same_bits(res["serial_ascending"][0], res["descending_q"][0])
     assert same_bits(res["serial_ascending"][1], res["atomic_nondet"][1])
