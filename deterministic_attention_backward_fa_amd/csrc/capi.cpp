@@ -99,8 +99,12 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
   if (s.S % bq != 0 || s.S % bkv != 0) return DETATTN_ERR_UNSUPPORTED;
   const int causal = mask == DETATTN_MASK_CAUSAL;
   const int n_q = s.S / bq, n_kv = s.S / bkv, r = bkv / bq;
+  // AUTO: the fastest deterministic schedule measured on MI355X. Causal:
+  // symmetric shift (descending for an odd KV-tile count). Full: descending on
+  // rings of one XCD (1-6% ahead of shift there), else shift (decided below).
+  const bool auto_full = sch == DETATTN_AUTO && !causal;
   if (sch == DETATTN_AUTO)
-    sch = !causal ? DETATTN_SHIFT : n_kv % 2 == 0 ? DETATTN_SYMMETRIC_SHIFT : DETATTN_DESCENDING_Q;
+    sch = !causal ? DETATTN_DESCENDING_Q : n_kv % 2 == 0 ? DETATTN_SYMMETRIC_SHIFT : DETATTN_DESCENDING_Q;
   if (sch == DETATTN_SHIFT && causal) return DETATTN_ERR_UNSUPPORTED;
   if (sch == DETATTN_SYMMETRIC_SHIFT && (!causal || n_kv % 2 != 0)) return DETATTN_ERR_UNSUPPORTED;
 
@@ -134,6 +138,11 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
     if (o.dispatch == 2) ring_sched = true;
     else if (o.dispatch == 0 && sch != DETATTN_ATOMIC_NONDET)
       ring_sched = xcd && grid % 8 == 0 && ring_pref <= grid / 8 && ip % ring_pref == 0;
+  }
+  if (auto_full && !ring_sched) {  // descending would fall back to the ticket counter: shift instead
+    sch = DETATTN_SHIFT;
+    sc.sch = kShift;
+    ring_sched = true;
   }
   if (ring_sched) {
     sc.G = ring_pref;

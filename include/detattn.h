@@ -66,10 +66,12 @@ typedef enum { DETATTN_MASK_FULL = 0, DETATTN_MASK_CAUSAL = 1 } detattn_mask_t;
  *                    summary 1). dK and dV remain deterministic.
  *  AUTO              the deterministic schedule measured fastest on MI355X
  *                    for the mask (the pages' future "dynamic scheduling",
- *                    explainer section 7): SHIFT for full masks,
- *                    SYMMETRIC_SHIFT for causal masks with an even number of
- *                    KV tiles, else DESCENDING_Q. The choice depends on the
- *                    shape only; detattn_plan_t.schedule reports it.
+ *                    explainer section 7): for causal masks SYMMETRIC_SHIFT
+ *                    (DESCENDING_Q for an odd number of KV tiles); for full
+ *                    masks DESCENDING_Q where its rings fit one XCD (1-6%
+ *                    ahead of SHIFT there), else SHIFT. The choice depends
+ *                    on the shape and the grid option only;
+ *                    detattn_plan_t.schedule reports it.
  */
 typedef enum {
   DETATTN_SERIAL_ASCENDING = 0,

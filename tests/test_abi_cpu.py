@@ -226,13 +226,15 @@ def test_ring_option_in_plan():
         da.detattn_bwd_plan(1, 16, 16384, 128, False, "shift", grid=256, ring_size=48, **kv64)
 
 
-@pytest.mark.parametrize("S,D,causal,want", [
-    (4096, 128, False, "shift"), (8192, 128, True, "symmetric_shift"), (2048, 64, True, "symmetric_shift"),
-    (16384, 128, False, "shift"), (384, 128, True, "descending_q"),   # 3 KV tiles: no symmetric pairing
-    (192, 128, True, "descending_q"),                                  # 64-row KV tiles (S % 128 != 0), 3 of them
+@pytest.mark.parametrize("S,D,causal,grid,want", [
+    (4096, 128, False, 256, "descending_q"), (8192, 128, True, 256, "symmetric_shift"),
+    (2048, 64, True, 256, "symmetric_shift"), (16384, 128, False, 256, "descending_q"),
+    (4096, 128, False, 100, "shift"),                                # no ring fits one XCD
+    (384, 128, True, 256, "descending_q"),                           # 3 KV tiles: no symmetric pairing
+    (192, 128, True, 256, "descending_q"),                           # 64-row KV tiles (S % 128 != 0), 3 of them
 ])
-def test_auto_schedule_resolves_from_the_shape(S, D, causal, want):
-    p = da.detattn_bwd_plan(1, 2, S, D, causal, "auto", grid=256)
+def test_auto_schedule_resolves_from_the_shape(S, D, causal, grid, want):
+    p = da.detattn_bwd_plan(1, 2, S, D, causal, "auto", grid=grid)
     assert da.SCHEDULE_NAMES[p["schedule"]] == want
-    q = da.detattn_bwd_plan(1, 2, S, D, causal, want, grid=256)
+    q = da.detattn_bwd_plan(1, 2, S, D, causal, want, grid=grid)
     assert p == q
