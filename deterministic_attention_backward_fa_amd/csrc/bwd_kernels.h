@@ -51,6 +51,7 @@ struct BwdArgs {
   Sched sc;
   int ticket_mode;     // 1: items claimed through the ticket counter in (head, item) order
   int ring, rings;     // static rings: workgroups per ring, rings in flight
+  int snake;           // static rings: odd rounds give slot g item kG + G-1-g (rank independent)
   int xcd_remap;       // place each ring on one XCD (workgroup w runs on XCD w % 8)
   long long timeout_ticks;  // s_memrealtime ticks (100 MHz)
   unsigned delay_seed;

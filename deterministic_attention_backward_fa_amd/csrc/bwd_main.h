@@ -618,9 +618,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   };
 
   // Ring mode: the ring takes heads ring_id, ring_id + rings, ...; inside a
-  // head, workgroup `slot` takes items slot, G + slot, ... (one per round,
-  // G = a.ring workgroups per ring).
-  int ring_bh = ring_id, ring_it = slot;
+  // head, workgroup `slot` takes one item per round of G = a.ring items: item
+  // kG + slot in round k.
+  // In snake order (a.snake) odd rounds hand the slots out in reverse, so a
+  // workgroup whose items shrink with j (descending, causal mask) gets a
+  // short item after a long one.
+  int ring_bh = ring_id, ring_k0 = 0;
+  bool ring_rev = false;
   for (;;) {
     long long gidx;
     if (a.ticket_mode) {
@@ -631,10 +635,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       if (gidx >= total_items) return;
     } else {
       if (ring_bh >= a.BH) return;
-      gidx = (long long)ring_bh * ipH + ring_it;
-      ring_it += a.ring;
-      if (ring_it >= ipH) {
-        ring_it = slot;
+      gidx = (long long)ring_bh * ipH + ring_k0 + (ring_rev ? a.ring - 1 - slot : slot);
+      ring_k0 += a.ring;
+      ring_rev = a.snake && !ring_rev;
+      if (ring_k0 >= ipH) {
+        ring_k0 = 0;
+        ring_rev = false;
         ring_bh += a.rings;
       }
     }
