@@ -224,23 +224,25 @@ def main():
     flops = counted_flops(B, H, S, D, causal)
     tile_opts = {k: v for k, v in (("block_q", args.block_q), ("block_kv", args.block_kv)) if v}
     results = {}
-    for sched in scheds:
-        log(f"[bench] timing {sched}: warmup {args.warmup}, steps {args.steps}")
+    def sched_opts(sched):
         opts = {"dq_mode": args.dq_mode} if (args.dq_mode != "default" and sched != "atomic_nondet") else {}
         opts.update(tile_opts)
         if args.ring_size and sched in ("shift", "symmetric_shift"):
             opts["ring_size"] = args.ring_size
         if args.dispatch != "default" and sched in ("serial_ascending", "descending_q", "atomic_nondet"):
             opts["dispatch"] = args.dispatch
+        return opts
+
+    for sched in scheds:
+        log(f"[bench] timing {sched}: warmup {args.warmup}, steps {args.steps}")
+        opts = sched_opts(sched)
         r = time_schedule(da, torch, ev, tensors, (B, H, S, D), causal, sched, args.steps, args.warmup, **opts)
         r["tflops"] = flops / (r["ms_per_step"] * 1e-3) / 1e12
         results[sched] = r
         log(f"[bench] {sched}: {r['ms_per_step']:.3f} ms/step, main {r['main_ms']:.3f} ms, "
             f"{r['tflops']:.1f} TFLOP/s, status {r['status']}, repeat bitwise {r['repeat_bitwise']}")
     head = results[headline]
-    plan_opts = dict(tile_opts)
-    if args.ring_size:
-        plan_opts["ring_size"] = args.ring_size
+    plan_opts = sched_opts(headline)
     plan = da.detattn_bwd_plan(B, H, S, D, causal, headline, **plan_opts)
     tiles = tiles_executed(plan, B, H, causal)
     algo_flops = 10.0 * plan["block_q"] * plan["block_kv"] * D * tiles
@@ -278,7 +280,7 @@ def main():
     if args.trace:
         from deterministic_attention_backward_fa_amd import trace as dtrace
 
-        recs, _ = dtrace.collect(da, tensors, causal, headline)
+        recs, _ = dtrace.collect(da, tensors, causal, headline, **sched_opts(headline))
         summ = dtrace.summarize(recs)
         log(f"[bench] trace {headline}: tile period median {summ['tile_period_median']:.0f} ticks, "
             f"{summ['early_turn_fraction'] * 100:.0f}% of tiles find their turn at the dS^T barrier "
