@@ -130,6 +130,11 @@ def test_invariance_grid_placement_delays(case):
             # same add mechanism gives the same bits
             variants += [dict(dispatch="ring"), dict(dispatch="ring", dq_mode=plan_mode_name(plan)),
                          dict(dispatch="ring", ring_size=1, grid=8)]
+            n_kv = plan["n_kv"]
+            if n_kv % 2 == 0 and n_kv >= 4:
+                # two workgroups per ring, several rounds: descending hands out odd rounds
+                # in reverse under a causal mask (snake order); the bits stay the same
+                variants.append(dict(dispatch="ring", ring_size=2, dq_mode=plan_mode_name(plan)))
         ring = plan["ring"]
         if ring:
             variants.append(dict(grid=ring))           # a single ring at a time
