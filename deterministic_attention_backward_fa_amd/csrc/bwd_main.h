@@ -653,21 +653,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
         __builtin_amdgcn_make_buffer_rsrc(a.dqacc + head_off, 0, a.S * D * 4, kBufferWord3);
 
 
-    for (int seg = 0; seg < sc.segments(); ++seg) {
-    const int t_begin = sc.seg_begin(it, seg), t_end = sc.seg_end(it, seg);
-    int j;
-    SegWalk cur = sc.walk(it, seg, j);  // at step t_begin
-    const int i0 = cur.i;
-    // ---- segment prologue: K_j, V_j and the first Q tile, synchronously ----
-    {
-      const unsigned char* gk = reinterpret_cast<const unsigned char*>(a.k + head_off + (long long)j * BKV * D);
-      const unsigned char* gv = reinterpret_cast<const unsigned char*>(a.v + head_off + (long long)j * BKV * D);
+    // K_j, V_j into their LDS tiles (asynchronous)
+    auto dma_kv = [&](long long kv_head, int kv_j) {
+      const unsigned char* gk = reinterpret_cast<const unsigned char*>(a.k + kv_head + (long long)kv_j * BKV * D);
+      const unsigned char* gv = reinterpret_cast<const unsigned char*>(a.v + kv_head + (long long)kv_j * BKV * D);
       for (int ins = w; ins < C::DMA_K; ins += 4) {
         const int go = dma_goff<C::NCH>(ins, lane);
         dma16(gk + go, smem + C::OFF_K + ins * 1024);
         dma16(gv + go, smem + C::OFF_V + ins * 1024);
       }
-    }
+    };
+    // The second column's K, V load while the first column's dK, dV go out
+    // (the epilogue's LDS staging lies below the K, V tiles).
+    static_assert(C::EPI_END <= C::OFF_K, "epilogue LDS overlaps the K/V tiles");
+
+    for (int seg = 0; seg < sc.segments(); ++seg) {
+    const int t_begin = sc.seg_begin(it, seg), t_end = sc.seg_end(it, seg);
+    int j;
+    SegWalk cur = sc.walk(it, seg, j);  // at step t_begin
+    const int i0 = cur.i;
+    // ---- segment prologue: K_j, V_j (the second column of a symmetric pair has
+    // them on their way already) and the first Q tile ----
+    if (seg == 0) dma_kv(head_off, j);
     dma_q(0, head_off, bhS, i0);
     wait_vm_all();
     __syncthreads();
@@ -1182,6 +1189,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       pend = nullptr;
     }
     __syncthreads();
+    // every wave's LDS reads and DMA of this column are done: the item's next
+    // column's K, V go out now, under the stores below
+    if (seg + 1 < sc.segments()) dma_kv(head_off, sc.seg_kv(it, seg + 1));
     {
       float* red = reinterpret_cast<float*>(smem);
       __bf16* sOut = reinterpret_cast<__bf16*>(smem + C::RED_BYTES);

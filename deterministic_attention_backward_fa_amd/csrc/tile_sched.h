@@ -109,6 +109,11 @@ struct Sched {
     return (sch == kSymmetricShift && seg == 0) ? n_q - it * r : item_len(it);
   }
 
+  // KV tile of segment `seg` of item `it`.
+  __host__ __device__ __forceinline__ int seg_kv(int it, int seg) const {
+    return (sch == kSymmetricShift && seg == 1) ? n_kv - 1 - it : it;
+  }
+
   // The t-th tile (0 <= t < item_len(it)) of item `it`.
   __host__ __device__ __forceinline__ void tile(int it, int t, int& i, int& j) const {
     switch (sch) {
