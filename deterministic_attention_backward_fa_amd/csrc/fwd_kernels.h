@@ -3,7 +3,10 @@
 // is owned by one wave and reduced in a fixed order.
 //
 // A workgroup of 4 waves owns 128 query rows (32 per wave, kept in registers)
-// and streams KV tiles of 64 rows through LDS. Each wave computes the scores
+// and streams KV tiles of 64 rows through LDS. At D = 64 the next tile's K, V
+// are loaded into registers while the current one is computed (at D = 128 the
+// extra registers cost more occupancy than the overlap gains). Under a causal
+// mask the grid runs the query blocks with the most KV tiles first. Each wave computes the scores
 // transposed, S^T = K Q^T, so that in the MFMA accumulator layout every lane
 // owns one query (its column) and the running max / sum of the online softmax
 // are per-lane scalars; O^T = V^T P^T then takes P^T straight from the
@@ -23,6 +26,10 @@ struct FwdCfg {
   static constexpr int KK = BKV / 16;   // K steps over a KV tile
   static constexpr int P = D + 8;       // LDS pitch
   static constexpr int LDS_BYTES = 2 * BKV * P * 2;
+  static constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
+  static constexpr int NPT = BKV * CPR / 256;    // chunks per thread per tile
+  static_assert(NPT * 256 == BKV * CPR, "tile chunks split evenly over 256 threads");
+  static constexpr bool PREFETCH = D <= 64;     // K, V of the next tile in registers
 };
 
 template <int D, bool CAUSAL>
@@ -34,7 +41,8 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(const __bf16* __restrict__ 
   __shared__ __attribute__((aligned(16))) __bf16 sV[C::BKV * C::P];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, c32 = lane & 31;
   const int bh = blockIdx.y;
-  const int q0 = blockIdx.x * C::BQ + 32 * w;  // this wave's first query row
+  const int qb = CAUSAL ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;  // query block
+  const int q0 = qb * C::BQ + 32 * w;  // this wave's first query row
   const long long head = (long long)bh * S * D;
   const float c1 = scale * kLog2e;
 
@@ -50,16 +58,31 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(const __bf16* __restrict__ 
   float m_run = -INFINITY, l_run = 0.f;  // log2 units; per lane = per query q0 + c32
   const int qi = q0 + c32;
 
-  const int kv_end = CAUSAL ? (blockIdx.x + 1) * C::BQ : S;
+  const int kv_end = CAUSAL ? (qb + 1) * C::BQ : S;
+  // thread tid moves chunks tid, tid + 256, ... of a tile: row cidx / CPR, chunk cidx % CPR
+  bf16x8 kr[C::NPT], vr[C::NPT];
+  auto load_tile = [&](int kv) {
+#pragma unroll
+    for (int x = 0; x < C::NPT; ++x) {
+      const int cidx = tid + 256 * x, r = cidx / C::CPR, c = cidx % C::CPR;
+      kr[x] = *reinterpret_cast<const bf16x8*>(k + head + (long long)(kv + r) * D + 8 * c);
+      vr[x] = *reinterpret_cast<const bf16x8*>(v + head + (long long)(kv + r) * D + 8 * c);
+    }
+  };
+  if constexpr (C::PREFETCH) load_tile(0);
   for (int kv0 = 0; kv0 < kv_end; kv0 += C::BKV) {
-    __syncthreads();
-    constexpr int CPR = D / 8;
-    for (int cidx = tid; cidx < C::BKV * CPR; cidx += 256) {
-      const int r = cidx / CPR, x = cidx % CPR;
-      lds_store16(sK + r * C::P + 8 * x, *reinterpret_cast<const bf16x8*>(k + head + (long long)(kv0 + r) * D + 8 * x));
-      lds_store16(sV + r * C::P + 8 * x, *reinterpret_cast<const bf16x8*>(v + head + (long long)(kv0 + r) * D + 8 * x));
+    __syncthreads();  // every wave is done with the previous tile in LDS
+    if constexpr (!C::PREFETCH) load_tile(kv0);
+#pragma unroll
+    for (int x = 0; x < C::NPT; ++x) {
+      const int cidx = tid + 256 * x, r = cidx / C::CPR, c = cidx % C::CPR;
+      lds_store16(sK + r * C::P + 8 * c, kr[x]);
+      lds_store16(sV + r * C::P + 8 * c, vr[x]);
     }
     __syncthreads();
+    if constexpr (C::PREFETCH) {
+      if (kv0 + C::BKV < kv_end) load_tile(kv0 + C::BKV);  // in flight during this tile's products
+    }
     if (CAUSAL && kv0 > q0 + 31) continue;  // whole tile masked for this wave
 
     // S^T = K Q^T : rows kv, columns q (lane)
