@@ -65,8 +65,8 @@ typedef enum { DETATTN_MASK_FULL = 0, DETATTN_MASK_CAUSAL = 1 } detattn_mask_t;
  *                    non-deterministic speed reference (explainer 2.1;
  *                    summary 1). dK and dV remain deterministic.
  *  AUTO              the deterministic schedule measured fastest on MI355X
- *                    for the mask (the pages' future "dynamic scheduling",
- *                    explainer section 7): for causal masks SYMMETRIC_SHIFT
+ *                    for the mask (the explainer's future work, section 7,
+ *                    chooses the schedule at run time): for causal masks SYMMETRIC_SHIFT
  *                    (DESCENDING_Q for an odd number of KV tiles); for full
  *                    masks DESCENDING_Q where its rings fit one XCD (1-6%
  *                    ahead of SHIFT there), else SHIFT. The choice depends
