@@ -13,6 +13,7 @@ import ctypes
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -61,8 +62,17 @@ class HipEvents:
         self.hip.hipEventDestroy(e)
 
 
+_C_TOKEN = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\])*"|\'(?:\\.|[^\'\\])*\'', re.S)
+
+
+def strip_c_comments(text):
+    """C/C++ source without its comments (string and character literals kept)."""
+    return _C_TOKEN.sub(lambda m: "" if m.group(0).startswith("/") else m.group(0), text)
+
+
 def kernel_source_hash():
-    """sha256 over the HIP library sources: identifies the kernel build a profile was taken on."""
+    """sha256 over the HIP library sources with their comments removed (comments
+    never reach the binary): identifies the kernel build a profile was taken on."""
     import glob
     import hashlib
 
@@ -72,7 +82,7 @@ def kernel_source_hash():
     files.append(os.path.join(ROOT, "include", "detattn.h"))
     for f in files:
         h.update(os.path.basename(f).encode())
-        h.update(open(f, "rb").read())
+        h.update(strip_c_comments(open(f).read()).encode())
     return h.hexdigest()
 
 
