@@ -33,6 +33,9 @@ CONFIGS = {
     "causal_b1_h16_s16384_d128_kv64": (1, 16, 16384, 128, True, 105, 100, {"block_q": 64, "block_kv": 64}),
     "full_b1_h16_s16384_d128": (1, 16, 16384, 128, False, 105, 100, {}),
     "causal_b1_h16_s16384_d128": (1, 16, 16384, 128, True, 105, 100, {}),
+    # the longest context here: 64k tokens (offsets and flag counts at their largest in this suite)
+    "full_b1_h4_s65536_d128": (1, 4, 65536, 128, False, 106, 2, {}),
+    "causal_b1_h4_s65536_d128": (1, 4, 65536, 128, True, 106, 2, {}),
 }
 
 
