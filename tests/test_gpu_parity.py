@@ -223,3 +223,23 @@ def test_ring_rounds_match_oracle_and_repeat(case):
                 assert same_bits(base[0], got[0]), var
             else:
                 assert rel_err(got[0].float().cpu().numpy(), base[0].float().cpu().numpy()) <= 1e-2
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"B{c[0]}H{c[1]}S{c[2]}D{c[3]}{'c' if c[4] else 'f'}")
+def test_gradient_identities_on_gpu_output(case):
+    """Rows of dS sum to zero, so the keys' dK sum to zero; rows of P sum to one,
+    so the keys' dV sum to the queries' dO. The bf16 outputs meet both up to
+    their rounding (relative 1e-2 of the summed magnitudes)."""
+    B, H, S, D, causal, seed, opts = case
+    _, (q, k, v, do, o, lse) = inputs(B, H, S, D, seed, causal)
+    for sched in schedules_for(causal):
+        say(f"[identities] {case} {sched}")
+        ws = da.alloc_workspace(B, H, S, D)
+        dq, dk, dv = da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule=sched, workspace=ws,
+                                               **opts)
+        assert da.detattn_device_status(ws) == 0
+        dk64, dv64, do64 = (t.double().cpu() for t in (dk, dv, do))
+        sk = dk64.sum(dim=2).abs()
+        assert torch.all(sk <= 1e-2 * dk64.abs().sum(dim=2) + 1e-6), sched
+        sv = (dv64.sum(dim=2) - do64.sum(dim=2)).abs()
+        assert torch.all(sv <= 1e-2 * dv64.abs().sum(dim=2) + 1e-6), sched

@@ -131,3 +131,21 @@ def test_partials_make_the_order_visible():
         assert len(diff) >= 5
         changed |= diff
     assert len(changed) >= 12
+
+
+def test_thousand_interleavings(model):
+    """1000 seeded interleavings across the dispatch forms, each ending with the
+    rank-order bits."""
+    configs = [("serial_ascending", True, 4, 2, 0, 0, 0, 3), ("descending_q", True, 4, 2, 1, 2, 2, 4),
+               ("shift", False, 4, 1, 1, 2, 2, 4), ("symmetric_shift", True, 4, 2, 1, 1, 2, 2)]
+    want = {}
+    for seed in range(1000):
+        sched, causal, n_kv, r, mode, G, rings, threads = configs[seed % 4]
+        snake = mode == 1 and causal and sched == "descending_q"
+        status, bits, walks, _, n_q = run_model(model, sched, causal, n_kv, r, 2, mode, G, rings, snake, threads,
+                                                seed)
+        assert status == "OK", (sched, seed)
+        key = seed % 4
+        if key not in want:
+            want[key] = expected_bits(walks, 2, n_q)
+        assert bits == want[key], (sched, seed)
