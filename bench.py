@@ -190,6 +190,8 @@ def main():
     ap.add_argument("--ring-size", type=int, default=0,
                     help="workgroups per ring of the shift schedules (0 = library default)")
     ap.add_argument("--trace", action="store_true", help="log the headline schedule's per-tile phase breakdown")
+    ap.add_argument("--no-companion", action="store_true",
+                    help="skip the full-mask companion workload of the default run")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -298,6 +300,35 @@ def main():
         for name, share in summ["share"].items():
             log(f"[bench]   {share * 100:5.1f}%  {summ['ticks'][name]:8.0f}  {name}")
         line["trace_share"] = {k: round(v, 4) for k, v in summ["share"].items()}
+    # The metric covers both masks: the default run also times the full-mask
+    # workload (every schedule) and reports it beside the causal headline.
+    default_run = (not args.shape and args.config == "causal_b1_h32_s8192_d128" and not args.only_headline
+                   and not tile_opts and not args.ring_size and args.dispatch == "default"
+                   and args.dq_mode == "default" and not args.schedule)
+    if default_run and not args.no_companion:
+        cB, cH, cS, cD, ccausal, cseed = CONFIGS["full_b2_h32_s4096_d128"]
+        log(f"[bench] companion full_b2_h32_s4096_d128: generating inputs (seed {cseed})")
+        cq, ck, cv, cdo = (t.cuda() for t in make_qkvdo(cB, cH, cS, cD, cseed))
+        co, clse = da.detattn_fwd(cq, ck, cv, causal=ccausal)
+        torch.cuda.synchronize()
+        cflops = counted_flops(cB, cH, cS, cD, ccausal)
+        cres = {}
+        for sched in ("shift", "serial_ascending", "descending_q", "atomic_nondet"):
+            r = time_schedule(da, torch, ev, (cq, ck, cv, co, cdo, clse), (cB, cH, cS, cD), ccausal, sched, args.steps,
+                              args.warmup)
+            r["tflops"] = cflops / (r["ms_per_step"] * 1e-3) / 1e12
+            cres[sched] = r
+            log(f"[bench] companion {sched}: {r['ms_per_step']:.3f} ms/step, {r['tflops']:.1f} TFLOP/s, "
+                f"status {r['status']}, repeat bitwise {r['repeat_bitwise']}")
+        ca = cres["atomic_nondet"]["tflops"]
+        line["full_mask"] = {
+            "workload": f"full attention backward B={cB} H={cH} S={cS} D={cD}", "schedule": "shift",
+            "value": round(cres["shift"]["tflops"], 2), "unit": "TFLOP/s",
+            "ratio_vs_atomic": round(cres["shift"]["tflops"] / ca, 4),
+            "schedules": {k_: {"tflops": round(r["tflops"], 2), "ms_per_step": round(r["ms_per_step"], 4),
+                               "repeat_bitwise": r["repeat_bitwise"], "ratio_vs_atomic": round(r["tflops"] / ca, 4)}
+                          for k_, r in cres.items()}}
+        del cq, ck, cv, cdo, co, clse
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: fp64 oracle on a bounded sample")
         line["cpu_baseline"] = cpu_baseline((B, H, S, D), causal, seed)
