@@ -190,6 +190,8 @@ def main():
     ap.add_argument("--ring-size", type=int, default=0,
                     help="workgroups per ring of the shift schedules (0 = library default)")
     ap.add_argument("--trace", action="store_true", help="log the headline schedule's per-tile phase breakdown")
+    ap.add_argument("--trace-gantt", action="store_true",
+                    help="with --trace: also print a text timeline of the traced workgroups")
     ap.add_argument("--no-companion", action="store_true",
                     help="skip the full-mask companion workload of the default run")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -300,6 +302,10 @@ def main():
         for name, share in summ["share"].items():
             log(f"[bench]   {share * 100:5.1f}%  {summ['ticks'][name]:8.0f}  {name}")
         line["trace_share"] = {k: round(v, 4) for k, v in summ["share"].items()}
+        if args.trace_gantt:
+            log(f"[bench] timeline of {headline} ('#' tile compute, 'w' waiting for the dQ turn, "
+                f"'e' column switch, ' ' idle; one row per workgroup):")
+            log(dtrace.gantt(recs))
     # The metric covers both masks: the default run also times the full-mask
     # workload (every schedule) and reports it beside the causal headline.
     default_run = (not args.shape and args.config == "causal_b1_h32_s8192_d128" and not args.only_headline

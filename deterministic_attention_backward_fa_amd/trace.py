@@ -81,3 +81,44 @@ def summarize(recs):
             "ticks": out, "workgroups": len(spans),
             "tile_period_median": float(np.median(periods)) if periods else 0.0,
             "early_turn_fraction": early / (early + late) if early + late else 0.0}
+
+
+# Gantt symbols per interval (phase a -> phase b); the rest is compute ('#')
+_GANTT = {(2, 3): "w", (5, 7): "e", (7, 6): "e", (6, 0): "e"}
+_PRIORITY = {" ": 0, "#": 1, "e": 2, "w": 3}
+
+
+def gantt(recs, width=100, max_rows=64):
+    """Text timeline of the traced workgroups: one row per workgroup, one column
+    per 1/width of the traced span. '#' computing a tile, 'w' waiting for a dQ
+    tile's turn, 'e' switching columns (dK/dV stores, the next K/V), ' ' idle.
+    A column shows the most telling state that falls into it (w > e > #).
+    The cycle counters of different compute units are not synchronized, so
+    every row starts at its workgroup's first record: the workgroups of the
+    persistent grid all start at launch, up to the launch skew."""
+    rows = [wg for wg in range(recs.shape[0]) if int(np.sum(recs[wg][:, 0] != 0)) > 1][:max_rows]
+    if not rows:
+        return ""
+    spans = []
+    for wg in rows:
+        r = recs[wg]
+        r = r[r[:, 0] != 0]
+        spans.append(int(r[-1, 0]) - int(r[0, 0]))
+    scale = width / max(1, max(spans))
+    lines = []
+    for wg in rows:
+        r = recs[wg]
+        r = r[r[:, 0] != 0]
+        t0 = int(r[0, 0])
+        t = r[:, 0].astype(np.int64)
+        ph = (r[:, 1] & 0xFF).astype(np.int64)
+        cells = [" "] * width
+        for x in range(len(r) - 1):
+            sym = _GANTT.get((int(ph[x]), int(ph[x + 1])), "#")
+            a = min(width - 1, int((t[x] - t0) * scale))
+            b = min(width - 1, int((t[x + 1] - t0) * scale))
+            for c in range(a, b + 1):
+                if _PRIORITY[sym] > _PRIORITY[cells[c]]:
+                    cells[c] = sym
+        lines.append(f"{wg:4d} |{''.join(cells)}|")
+    return "\n".join(lines)
