@@ -117,7 +117,7 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
   const int ip = sc.items_per_head();
   const int ring_pref = o.ring_size ? o.ring_size : default_ring(ip);
   const long long BH = (long long)s.B * s.H;
-  const long long items = BH * sc.items_per_head();
+  const long long items = BH * ip;
   int capacity = 0;  // co-resident workgroups
   int cus = 0;
   if (o.grid == 0) {
@@ -145,14 +145,12 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
     ring_sched = true;
   }
   if (ring_sched) {
-    sc.G = ring_pref;
-    if (ip % sc.G != 0) return DETATTN_ERR_UNSUPPORTED;
-  }
-  if (ring_sched) {
     // Every ring (G workgroups sharing one head's items) must be co-resident.
     // With the XCD remap a ring occupies consecutive slots of one XCD
     // (workgroup w runs on XCD w % 8), so its dQ hand-offs stay inside that
     // XCD's L2.
+    sc.G = ring_pref;
+    if (ip % sc.G != 0) return DETATTN_ERR_UNSUPPORTED;
     ring = sc.G;
     if (grid < ring) return DETATTN_ERR_UNSUPPORTED;
     if (xcd && grid % 8 == 0 && ring <= grid / 8) {
