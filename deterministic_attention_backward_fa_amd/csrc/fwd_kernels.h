@@ -6,9 +6,10 @@
 // and streams KV tiles of 64 rows through LDS. At D = 64 the next tile's K, V
 // are loaded into registers while the current one is computed (at D = 128 the
 // extra registers cost more occupancy than the overlap gains). The D = 128
-// instances are held to 168 registers, three waves per SIMD (the causal one
-// spills a few registers there and is still faster than at two waves). Under a
-// causal mask the grid runs the query blocks with the most KV tiles first. Each wave computes the scores
+// instances are held to 168 registers, three waves per SIMD, and the D = 64
+// ones to 128, four waves (the causal instances spill a few registers there
+// and are still faster than with fewer waves). Under a causal mask the grid
+// runs the query blocks with the most KV tiles first. Each wave computes the scores
 // transposed, S^T = K Q^T, so that in the MFMA accumulator layout every lane
 // owns one query (its column) and the running max / sum of the online softmax
 // are per-lane scalars; O^T = V^T P^T then takes P^T straight from the
@@ -35,7 +36,7 @@ struct FwdCfg {
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 3 : 1))) void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 3 : 4))) void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                                      const __bf16* __restrict__ v, __bf16* __restrict__ o,
                                                      float* __restrict__ lse, int S, float scale) {
   using C = FwdCfg<D>;
