@@ -140,8 +140,10 @@ def time_schedule(da, torch, ev, tensors, shape, causal, sched, steps, warmup, *
         ev.destroy(e)
     status = da.detattn_device_status(ws)
     same = all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(ref, out))
-    return {"ms_per_step": total_ms / steps, "main_ms": sum(main_ms) / steps, "status": status,
-            "repeat_bitwise": bool(same)}
+    srt = sorted(main_ms)
+    return {"ms_per_step": total_ms / steps, "main_ms": sum(main_ms) / steps,
+            "main_ms_median": srt[len(srt) // 2] if len(srt) % 2 else 0.5 * (srt[len(srt) // 2 - 1] + srt[len(srt) // 2]),
+            "main_ms_min": srt[0], "status": status, "repeat_bitwise": bool(same)}
 
 
 def cpu_baseline(cfg_shape, causal, seed, budget_s=15.0, max_heads=64):
@@ -281,7 +283,8 @@ def main():
                    "grid": plan["grid"], "ring": plan["ring"], "parallelism": "single GPU"},
         "ratio_vs_atomic": round(head["tflops"] / atomic["tflops"], 4) if atomic else None,
         "schedules": {s: {"tflops": round(r["tflops"], 2), "ms_per_step": round(r["ms_per_step"], 4),
-                          "main_ms": round(r["main_ms"], 4), "repeat_bitwise": r["repeat_bitwise"],
+                          "main_ms": round(r["main_ms"], 4), "main_ms_median": round(r["main_ms_median"], 4),
+                          "main_ms_min": round(r["main_ms_min"], 4), "repeat_bitwise": r["repeat_bitwise"],
                           "ratio_vs_atomic": round(r["tflops"] / atomic["tflops"], 4) if atomic else None}
                       for s, r in results.items()},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -289,7 +292,9 @@ def main():
                      "traffic": traffic["hbm_bytes_per_launch"] if traffic else None,
                      "traffic_detail": traffic,
                      "kernel": "bwd_main_kernel", "algorithmic_flops_per_launch": algo_flops,
-                     "avg_launch_ms": round(head["main_ms"], 4)},
+                     "avg_launch_ms": round(head["main_ms"], 4),
+                     "median_launch_ms": round(head["main_ms_median"], 4),
+                     "min_launch_ms": round(head["main_ms_min"], 4)},
     }
     if args.trace:
         from deterministic_attention_backward_fa_amd import trace as dtrace
