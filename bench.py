@@ -146,6 +146,17 @@ def time_schedule(da, torch, ev, tensors, shape, causal, sched, steps, warmup, *
             "main_ms_min": srt[0], "status": status, "repeat_bitwise": bool(same)}
 
 
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(cfg_shape, causal, seed, budget_s=15.0, max_heads=64):
     """The fp64 oracle (unchanged) on whole heads of the same workload until ~budget_s of CPU time."""
     import torch
@@ -167,6 +178,7 @@ def cpu_baseline(cfg_shape, causal, seed, budget_s=15.0, max_heads=64):
         log(f"[cpu_baseline] oracle head {heads}: {elapsed:.1f} s cumulative")
     flops = counted_flops(1, heads, S, D, causal)
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": ref.max_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"fp64 oracle backward (forward statistics recomputed) on {heads} of {B * H} heads "
                       f"(S={S}, D={D}, {'causal' if causal else 'full'}), {elapsed:.1f} s wall",
             "seconds": elapsed}
@@ -282,6 +294,9 @@ def main():
                    "schedule": headline, "block_q": plan["block_q"], "block_kv": plan["block_kv"],
                    "grid": plan["grid"], "ring": plan["ring"], "parallelism": "single GPU"},
         "ratio_vs_atomic": round(head["tflops"] / atomic["tflops"], 4) if atomic else None,
+        "ratio_vs_atomic_note": ("the atomic reference is bound by device-scope fp32 atomic adds (about 1.35 TB/s "
+                                 "of dQ partials), so this ratio says little about the cost of ordering; "
+                                 "roofline.frac is the binding target"),
         "schedules": {s: {"tflops": round(r["tflops"], 2), "ms_per_step": round(r["ms_per_step"], 4),
                           "main_ms": round(r["main_ms"], 4), "main_ms_median": round(r["main_ms_median"], 4),
                           "main_ms_min": round(r["main_ms_min"], 4), "repeat_bitwise": r["repeat_bitwise"],

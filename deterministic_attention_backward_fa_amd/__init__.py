@@ -20,7 +20,7 @@ SCHEDULE_NAMES = {v: k for k, v in SCHEDULES.items()}
 DQ_MODES = {"default": 0, "rmw": 1, "atomic": 2, "xcd_local": 3}
 DISPATCH = {"default": 0, "ticket": 1, "ring": 2}
 STATUS = {0: "OK", 1: "ERR_INVALID_ARG", 2: "ERR_UNSUPPORTED", 3: "ERR_WORKSPACE", 4: "ERR_HIP",
-          5: "ERR_DEVICE_TIMEOUT", 6: "ERR_DEVICE_PLACEMENT"}
+          5: "ERR_DEVICE_TIMEOUT", 6: "ERR_DEVICE_PLACEMENT (not returned any more)"}
 
 
 class DetAttnError(RuntimeError):
@@ -170,9 +170,11 @@ def alloc_workspace(B, H, S, D, device="cuda"):
 
 
 def attn_bwd_deterministic(q, k, v, o, dout, lse, causal=False, schedule="serial_ascending", scale=None,
-                           workspace=None, out=None, stream=None, **opts):
+                           workspace=None, out=None, stream=None, check=False, **opts):
     """dQ, dK, dV (bf16) of softmax attention. `opts` are BwdOptions fields
-    (block_q, block_kv, grid, xcd_remap, dq_mode, debug_delay_seed, timeout_us, debug_skip_signal, ring_size, dispatch)."""
+    (block_q, block_kv, grid, xcd_remap, dq_mode, debug_delay_seed, timeout_us, debug_skip_signal, ring_size, dispatch).
+    check=True synchronises the stream after the call and raises DetAttnError if the
+    workspace's device status reports an error (detattn_device_status)."""
     B, H, S, D = q.shape
     for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
         _check_tensor(n, t, torch.bfloat16, (B, H, S, D))
@@ -195,6 +197,10 @@ def attn_bwd_deterministic(q, k, v, o, dout, lse, causal=False, schedule="serial
         st = lib().attn_bwd_deterministic(*args, _stream(stream))
     if st != 0:
         raise DetAttnError(st, f"attn_bwd_deterministic({schedule})")
+    if check:
+        st = detattn_device_status(workspace, stream)
+        if st != 0:
+            raise DetAttnError(st, f"attn_bwd_deterministic({schedule}) on the device")
     return dq, dk, dv
 
 

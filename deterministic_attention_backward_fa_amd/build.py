@@ -6,6 +6,7 @@ Each translation unit is compiled to an object in parallel, then linked into
 """
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -45,6 +46,30 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
+_REMARK = re.compile(r"remark: +(Function Name|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]|"
+                     r"SGPRs Spill|VGPRs Spill|LDS Size \[bytes/block\]): (\S+)")
+
+
+def resource_usage(src: str = "bwd_d128.hip", extra=()):
+    """Per-kernel register and spill counts of one translation unit, from the
+    compiler's kernel-resource-usage remarks: {mangled name: {field: value}}."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    obj = os.path.join(BUILD_DIR, "resource_" + os.path.basename(src) + ".o")
+    cmd = ([hipcc(), "-c", "-x", "hip", os.path.join(CSRC, src), "-o", obj] + COMMON + PER_SOURCE.get(src, []) +
+           list(extra) + ["-Rpass-analysis=kernel-resource-usage"])
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stderr}")
+    out, cur = {}, None
+    for m in _REMARK.finditer(r.stderr):
+        key, val = m.group(1).split(" [")[0], m.group(2)
+        if key == "Function Name":
+            cur = out.setdefault(val, {})
+        elif cur is not None:
+            cur[key] = int(val)
+    return out
+
+
 def build(extra_flags=(), verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
@@ -61,4 +86,9 @@ def build(extra_flags=(), verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(extra_flags=sys.argv[1:], verbose=True)
+    if sys.argv[1:2] == ["--resource-usage"]:
+        # python -m deterministic_attention_backward_fa_amd.build --resource-usage [source.hip]
+        for name, f in resource_usage(*(sys.argv[2:3] or ["bwd_d128.hip"])).items():
+            print(name, " ".join(f"{k}={v}" for k, v in f.items()))
+    else:
+        build(extra_flags=sys.argv[1:], verbose=True)

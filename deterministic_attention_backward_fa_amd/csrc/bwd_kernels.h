@@ -45,14 +45,16 @@ struct BwdArgs {
   __bf16* dv;
   int* flags;          // one int per (head, Q tile), stride kFlagInts
   unsigned* ticket;    // dynamic item counter
-  unsigned* err;       // device error word
+  unsigned* err;       // error bits of this call (workspace header, kHdrAbort)
+  unsigned* sticky;    // error bits kept until the status is read (kHdrSticky)
+  unsigned* xcd_reg;   // XCD registration: 8 per-XCD counters, then the arrival count
   int BH, S;
   float scale;
   Sched sc;
   int ticket_mode;     // 1: items claimed through the ticket counter in (head, item) order
   int ring, rings;     // static rings: workgroups per ring, rings in flight
   int snake;           // static rings: odd rounds give slot g item kG + G-1-g (rank independent)
-  int xcd_remap;       // place each ring on one XCD (workgroup w runs on XCD w % 8)
+  int xcd_remap;       // rings of one XCD: membership from the XCD each workgroup runs on
   long long timeout_ticks;  // s_memrealtime ticks (100 MHz)
   unsigned delay_seed;
   int skip_item;       // testing: global item index whose first signal is withheld, or -1
@@ -73,16 +75,25 @@ __device__ __forceinline__ unsigned hash3(unsigned a, unsigned b, unsigned c) {
 
 __device__ __forceinline__ long long now_ticks() { return (long long)__builtin_amdgcn_s_memrealtime(); }
 
+// A device-side failure: the call's abort word (every later wait of the call
+// gives up at once) and the sticky status word (read by detattn_device_status).
+__device__ __forceinline__ void report_error(const BwdArgs& a, unsigned bits) {
+  __hip_atomic_fetch_or(a.err, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_fetch_or(a.sticky, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ---------------------------------------------------------------------------
 // Preprocess: D_i = sum_d dO[i,d] * O[i,d] (fp32, fixed order); the main
-// kernel's accumulator initial values -D_i and -LSE_i / scale; zero the flags,
-// the ticket and the error word, and (unordered mode) the dQ accumulator.
+// kernel's accumulator initial values -D_i and -LSE_i * log2(e); zero the
+// flags and the per-call header words (ticket, abort word, XCD registration),
+// initialise the sticky status word on a workspace's first use, and
+// (unordered mode) zero the dQ accumulator.
 // 16 threads per row, each summing 8 contiguous products in order, then a
 // fixed butterfly across the 16 lanes.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dout,
-                                                      const float* __restrict__ lse, float inv_scale,
+                                                      const float* __restrict__ lse,
                                                       float* __restrict__ nlse, float* __restrict__ ndelta,
                                                       long long rows, int* flags,
                                                       long long n_flags, unsigned* header, float* dqacc,
@@ -104,10 +115,17 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
   for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, TPR);
   if (row < rows && part == 0) {
     ndelta[row] = -acc;
-    nlse[row] = -lse[row] * inv_scale;
+    nlse[row] = -lse[row] * kLog2e;
   }
   for (long long f = gtid; f < n_flags; f += gsz) flags[f * kFlagInts] = 0;
-  if (gtid < 64) header[gtid] = 0;
+  if (gtid < kHdrZeroWords) header[gtid] = 0;
+  if (gtid == 0) {
+    unsigned long long* tag = reinterpret_cast<unsigned long long*>(header + kHdrTag);
+    if (*tag != kStickyTag) {
+      header[kHdrSticky] = 0;
+      *tag = kStickyTag;
+    }
+  }
   if (dqacc) {
     f32x4 z = {0.f, 0.f, 0.f, 0.f};
     for (long long x = gtid; x < dqacc_n4; x += gsz) reinterpret_cast<f32x4*>(dqacc)[x] = z;

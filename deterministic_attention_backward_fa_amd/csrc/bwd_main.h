@@ -18,10 +18,12 @@
 // tile_sched.h decide the order). dQ = scale * accumulator is rounded to bf16
 // by the convert kernel; dK is scaled in the epilogue.
 //
-// Accumulator initial values carry the row terms: the S accumulator of row q
-// starts at -LSE_q/scale (so P = exp2(scale*log2e * acc)) and the dP
-// accumulator at -D_q (so dS = P * acc). Causal masking sets the S initial
-// value to -inf above the diagonal, on diagonal tiles only.
+// Accumulator initial values carry the row terms: the S product uses K_j
+// scaled by scale*log2(e) (rounded to bf16 once per column) and its
+// accumulator of row q starts at -LSE_q*log2(e), so P = exp2(acc) with no
+// multiply per element; the dP accumulator starts at -D_q (so dS = P * acc).
+// Causal masking sets the S initial value to -inf above the diagonal, on
+// diagonal tiles only.
 //
 // Instruction streams of one tile (one wave runs per SIMD, so MFMA, VALU,
 // LDS and memory work overlap only when interleaved in the wave's own stream):
@@ -517,7 +519,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   const int wq = w / C::NKVW;
   const int nbq = (w % C::DGRP) * C::DW;    // dQ: this wave's first D block
   const int mq0 = (w / C::DGRP) * C::MQD;  // dQ: first 32-row block
-  const float c1 = a.scale * kLog2e;
+  const float c1 = a.scale * kLog2e;  // K scale of the S product (exp2 domain)
   const Sched sc = a.sc;
   const int ipH = sc.items_per_head();
   const long long total_items = (long long)a.BH * ipH;
@@ -558,10 +560,60 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
   for (int x = 0; x < C::DMA_QW; ++x) goffQ[x] = dma_goff<C::NCH>(w + 4 * x, lane);
 
-  int ring_id = 0, slot = 0;
+  int ring_id = 0, slot = 0, n_rings = a.rings;
   if (!a.ticket_mode) {
     const int wg = blockIdx.x;
-    if (a.xcd_remap) {
+    if (kLocal && a.xcd_remap) {
+      // Rings of one XCD (their dQ hand-offs stay in that XCD's L2): a
+      // workgroup joins a ring of the XCD it runs on, read from the hardware,
+      // so the mode's correctness does not rest on how workgroups are
+      // dispatched to XCDs. Every workgroup registers (the grid is
+      // co-resident: cooperative launch), then each XCD forms
+      // floor(count / G) rings from its registered workgroups in arrival
+      // order; rings are numbered round-major over the XCDs (with equal counts,
+      // ring k*8 + x is the k-th ring of XCD x). Surplus workgroups exit.
+      if (tid == 0) {
+        unsigned xcc;
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+        xcc &= 7;
+        const int my = (int)__hip_atomic_fetch_add(a.xcd_reg + xcc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(a.xcd_reg + 8, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        int rid = -1, sl = 0, nr = 0;
+        const long long t0 = now_ticks();
+        bool all = true;
+        while (__hip_atomic_load(a.xcd_reg + 8, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < gridDim.x) {
+          __builtin_amdgcn_s_sleep(1);
+          if (now_ticks() - t0 > a.timeout_ticks ||
+              __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+            report_error(a, kErrTimeout);
+            all = false;
+            break;
+          }
+        }
+        if (all) {
+          int rx[8];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            rx[x] = (int)__hip_atomic_load(a.xcd_reg + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) / a.ring;
+            nr += rx[x];
+          }
+          const int k = my / a.ring;
+          sl = my % a.ring;
+          if (k < rx[xcc]) {
+            rid = 0;
+#pragma unroll
+            for (int x = 0; x < 8; ++x) rid += (rx[x] < k ? rx[x] : k) + ((x < (int)xcc && rx[x] > k) ? 1 : 0);
+          }
+        }
+        sMisc[1] = rid;
+        sMisc[2] = sl;
+        sMisc[3] = nr;
+      }
+      __syncthreads();
+      ring_id = __builtin_amdgcn_readfirstlane(sMisc[1]);
+      slot = __builtin_amdgcn_readfirstlane(sMisc[2]);
+      n_rings = __builtin_amdgcn_readfirstlane(sMisc[3]);
+    } else if (a.xcd_remap) {
       const int x = wg & 7, u = wg >> 3;
       ring_id = (u / a.ring) * 8 + x;
       slot = u % a.ring;
@@ -569,20 +621,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       ring_id = wg / a.ring;
       slot = wg % a.ring;
     }
-    if (ring_id >= a.rings) return;
-    if constexpr (kLocal) {
-      // the ring placement assumes workgroup w runs on XCD w % 8: verify it
-      unsigned xcc;
-      asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-      if (tid == 0 && (int)(xcc & 0xF) != (wg & 7))
-        __hip_atomic_fetch_or(a.err, (unsigned)kErrPlacement, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (ring_id < 0 || ring_id >= n_rings) return;
   }
 
-  auto ld16 = [&](int off) -> bf16x8 { return *reinterpret_cast<const bf16x8*>(smem + off); };
   const uint32_t lbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)smem;
   const uint32_t aS = lbase + oS, aS_hi = lbase + oS_hi;
-  auto ldtr = [&](int off) -> bf16x4 { return lds_read_tr(reinterpret_cast<const __bf16*>(smem + off)); };
 
   // Q, dO and the row terms of Q tile i -> buffer b (asynchronous).
   auto dma_q = [&](int b, long long head_off, long long bhS, int i) {
@@ -641,7 +684,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       if (ring_k0 >= ipH) {
         ring_k0 = 0;
         ring_rev = false;
-        ring_bh += a.rings;
+        ring_bh += n_rings;
       }
     }
     const int bh = (int)(gidx / ipH);
@@ -691,7 +734,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       u32x2 tlo[NT], thi[NT];
       static_for<0, C::KD>([&](auto sc_) {
         constexpr int s = decltype(sc_)::value;
-        kq[s] = lds_ld16_agpr<32 * s>(ak);
+        kq[s] = lds_ld16_asm<32 * s>(ak);  // scaled below, then moved to AGPRs
         vq[s] = lds_ld16_agpr<32 * s>(av);
       });
       static_for<0, NT>([&](auto xc) {
@@ -703,7 +746,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       static_for<0, C::KD>([&](auto sc_) {
         constexpr int s = decltype(sc_)::value;
         constexpr int after_k = 2 * (C::KD - 1 - s) + 1 + 2 * NT;
-        lgkm_wait_agpr<cmin(after_k, 15)>(kq[s]);  // more loads than the counter holds: 15 is still safe
+        lgkm_wait<cmin(after_k, 15)>(kq[s]);  // more loads than the counter holds: 15 is still safe
         lgkm_wait_agpr<cmin(after_k - 1, 15)>(vq[s]);
       });
       static_for<0, NT>([&](auto xc) {
@@ -714,7 +757,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       });
 #pragma unroll
       for (int s = 0; s < C::KD; ++s) {
-        kB[s] = as_bf16x8(kq[s]);
+        // K_j * scale * log2(e), rounded to bf16 (RNE): the S accumulator is then
+        // directly the exp2 argument
+        const bf16x8 kraw = as_bf16x8(kq[s]);
+#pragma unroll
+        for (int t = 0; t < 8; t += 2) {
+          const bf16x2 p2 = cvt2((float)kraw[t] * c1, (float)kraw[t + 1] * c1);
+          kB[s][t] = p2[0];
+          kB[s][t + 1] = p2[1];
+        }
         vB[s] = as_bf16x8(vq[s]);
         pin_agpr(kB[s]);
         pin_agpr(vB[s]);
@@ -858,7 +909,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
         constexpr int q4 = u / 5, pos = u % 5;
         if constexpr (pos < 4) {
           constexpr int r = 4 * q4 + pos;
-          pv[r] = __builtin_amdgcn_exp2f(c1 * sAcc[e][r]);
+          pv[r] = __builtin_amdgcn_exp2f(sAcc[e][r]);
           dv[r] = pv[r] * pAcc[e][r];
           if constexpr (r & 1) {
             constexpr int sq = 2 * e + (r >> 3), sl = (r - 1) & 7;
@@ -1042,7 +1093,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
               if (((++spins) & 255) == 0) {
                 if (now_ticks() - t0 > a.timeout_ticks ||
                     __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
-                  __hip_atomic_fetch_or(a.err, (unsigned)kErrTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                  report_error(a, kErrTimeout);
                   break;
                 }
               }

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 
@@ -16,10 +17,12 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Sizes the kernels index with 32-bit integers: every element of a call
+// (B*H*S*D) and the bytes of one head's fp32 dQ accumulator (S*D*4).
 bool shape_ok(const detattn_shape_t& s) {
   if (s.B < 0 || s.H < 0 || s.S < 0 || s.D <= 0) return false;
   const long long n = (long long)s.B * s.H * s.S * s.D;
-  return n < (1LL << 31);
+  return n < (1LL << 31) && (long long)s.S * s.D * 4 < (1LL << 31);
 }
 
 bool is_empty(const detattn_shape_t& s) { return s.B == 0 || s.H == 0 || s.S == 0; }
@@ -51,18 +54,54 @@ bool tiles_built(int D, int bq, int bkv) {
   return false;
 }
 
-// Workgroups of one XCD on MI355X (256 compute units in 8 XCDs).
+// MI355X: 256 compute units in 8 XCDs, one main-kernel workgroup each.
+constexpr int kXcds = 8;
 constexpr int kXcdSlots = 32;
+// Measured cost of dQ hand-offs that leave one XCD's L2, relative to rings of
+// one XCD: one ring per head spanning XCDs ran 2.0-2.5x slower (16k tokens),
+// the ticket counter with device-scope ordered adds 1.6-1.9x slower.
+constexpr double kCrossRingCost = 2.0;
+constexpr double kTicketCost = 1.8;
 
-// Default ring size of the shift schedules: the head's items if they fit one
-// XCD, else the largest divisor of the item count that does (the ring then
-// takes the items in rounds). It depends on the shape only, so the
-// accumulation order, and with it every bit of dQ, does not depend on the grid.
-int default_ring(int items_per_head) {
-  if (items_per_head <= kXcdSlots) return items_per_head;
-  for (int g = kXcdSlots; g > 1; --g)
-    if (items_per_head % g == 0) return g;
-  return 1;
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+// Makespan, in item times, of BH heads of ip items each on rings of G
+// workgroups confined to one XCD, with `slots_per_xcd` workgroups per XCD: each
+// XCD runs floor(slots / G) rings (no more than its share of the heads needs),
+// and a ring takes its heads one after the other, ip / G rounds each.
+double local_ring_cost(long long BH, int ip, int G, int slots_per_xcd) {
+  const long long per_xcd = slots_per_xcd / G;
+  if (per_xcd == 0 || ip % G != 0) return 1e300;
+  const long long rings = kXcds * std::min(per_xcd, ceil_div(BH, kXcds));
+  return (double)ceil_div(BH, rings) * (ip / G);
+}
+
+// The same for one ring per head as wide as its item count (the pages' single
+// round), spanning XCDs, with `slots` workgroups in all.
+double cross_ring_cost(long long BH, int ip, int slots) {
+  const long long rings = std::min<long long>(slots / ip, BH);
+  if (rings == 0) return 1e300;
+  return (double)ceil_div(BH, rings) * kCrossRingCost;
+}
+
+// Default ring size G of the shift schedules: the divisor of the item count
+// up to one XCD's 32 workgroups (or, when none keeps enough of the chip busy,
+// the whole item count on a ring spanning XCDs) with the shortest makespan
+// above, larger G on ties (measured faster at equal makespan). It is chosen for
+// MI355X's nominal 8 x 32 workgroups and depends on the shape only: G sets the
+// accumulation order, so every bit of dQ is independent of the grid.
+int default_ring(long long BH, int ip) {
+  int best = 1;
+  double best_cost = 1e301;
+  for (int g = std::min(ip, kXcdSlots); g >= 1; --g) {
+    const double c = local_ring_cost(BH, ip, g, kXcdSlots);
+    if (c < best_cost) {
+      best = g;
+      best_cost = c;
+    }
+  }
+  if (ip > kXcdSlots && cross_ring_cost(BH, ip, kXcds * kXcdSlots) < best_cost) best = ip;
+  return best;
 }
 
 int device_cus() {
@@ -115,7 +154,6 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
 
   Sched sc{(int)sch, causal, n_q, n_kv, r, 0};
   const int ip = sc.items_per_head();
-  const int ring_pref = o.ring_size ? o.ring_size : default_ring(ip);
   const long long BH = (long long)s.B * s.H;
   const long long items = BH * ip;
   int capacity = 0;  // co-resident workgroups
@@ -134,21 +172,42 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
   // The atomic reference stays on the ticket counter with device-scope adds
   // unless asked: its adds confined to one XCD's L2 measured slower.
   bool ring_sched = sch == DETATTN_SHIFT || sch == DETATTN_SYMMETRIC_SHIFT;
+  int ring_pref = o.ring_size;
   if (sch == DETATTN_SERIAL_ASCENDING || sch == DETATTN_DESCENDING_Q || sch == DETATTN_ATOMIC_NONDET) {
+    // rank = KV tile whatever the dispatch: the ring size may follow the grid
+    const bool local_fits = xcd && grid % kXcds == 0 && grid >= kXcds;
+    if (!ring_pref) {
+      ring_pref = 1;
+      double best = 1e301;
+      const int slots = local_fits ? grid / kXcds : 0;
+      for (int g = std::min(ip, std::max(slots, 1)); g >= 1; --g) {
+        const double c = local_fits ? local_ring_cost(BH, ip, g, slots) : 1e300;
+        if (c < best) {
+          best = c;
+          ring_pref = g;
+        }
+      }
+      if (o.dispatch == 0 && sch != DETATTN_ATOMIC_NONDET)
+        ring_sched = local_fits && best <= (double)ceil_div(items, grid) * kTicketCost;
+    } else if (o.dispatch == 0 && sch != DETATTN_ATOMIC_NONDET) {
+      ring_sched = local_fits && ring_pref <= grid / kXcds && ip % ring_pref == 0;
+    }
     if (o.dispatch == 2) ring_sched = true;
-    else if (o.dispatch == 0 && sch != DETATTN_ATOMIC_NONDET)
-      ring_sched = xcd && grid % 8 == 0 && ring_pref <= grid / 8 && ip % ring_pref == 0;
+  } else if (!ring_pref) {
+    ring_pref = default_ring(BH, ip);
   }
   if (auto_full && !ring_sched) {  // descending would fall back to the ticket counter: shift instead
     sch = DETATTN_SHIFT;
     sc.sch = kShift;
     ring_sched = true;
+    ring_pref = o.ring_size ? o.ring_size : default_ring(BH, ip);
   }
   if (ring_sched) {
     // Every ring (G workgroups sharing one head's items) must be co-resident.
-    // With the XCD remap a ring occupies consecutive slots of one XCD
-    // (workgroup w runs on XCD w % 8), so its dQ hand-offs stay inside that
-    // XCD's L2.
+    // With rings of one XCD, each XCD runs `rings / 8` of them, so their dQ
+    // hand-offs stay inside that XCD's L2: in the XCD-local modes workgroups
+    // join rings by the XCD the hardware reports, otherwise workgroup w is
+    // taken to run on XCD w % 8 (a placement only performance depends on).
     sc.G = ring_pref;
     if (ip % sc.G != 0) return DETATTN_ERR_UNSUPPORTED;
     ring = sc.G;
@@ -217,7 +276,7 @@ const char* detattn_status_string(int status) {
     case DETATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case DETATTN_ERR_HIP: return "HIP runtime error";
     case DETATTN_ERR_DEVICE_TIMEOUT: return "ordered dQ wait timed out on the device";
-    case DETATTN_ERR_DEVICE_PLACEMENT: return "a workgroup ran on an unexpected XCD (XCD-local dQ mode)";
+    case DETATTN_ERR_DEVICE_PLACEMENT: return "a workgroup ran on an unexpected XCD (no longer reported)";
     default: return "unknown status";
   }
 }
@@ -271,7 +330,7 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
   const long long elems = rows * s.D;
   const bool unordered = P.dqm_internal == kDqUnordered || P.dqm_internal == kDqUnorderedLocal;
 
-  hipError_t e = launch_pre(s.D, static_cast<const __bf16*>(o), static_cast<const __bf16*>(dout), lse, 1.f / s.softmax_scale,
+  hipError_t e = launch_pre(s.D, static_cast<const __bf16*>(o), static_cast<const __bf16*>(dout), lse,
                             nlse, ndelta, rows, flags,
                             BH * P.pub.n_q, header, unordered ? dqacc : nullptr, elems, st_);
   if (e != hipSuccess) return DETATTN_ERR_HIP;
@@ -288,8 +347,11 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
   a.dk = static_cast<__bf16*>(dk);
   a.dv = static_cast<__bf16*>(dv);
   a.flags = flags;
-  a.ticket = header;
-  a.err = header + 16;
+  a.ticket = header + kHdrTicket;
+  a.err = header + kHdrAbort;
+  a.sticky = header + kHdrSticky;
+  a.xcd_reg = header + kHdrXcdCount;
+  static_assert(kHdrXcdArrived == kHdrXcdCount + 8, "registration words");
   a.BH = (int)BH;
   a.S = s.S;
   a.scale = s.softmax_scale;
@@ -342,11 +404,16 @@ int attn_bwd_deterministic(const void* q, const void* k, const void* v, const vo
 int detattn_device_status(void* workspace, void* stream) {
   if (!workspace) return DETATTN_ERR_INVALID_ARG;
   if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return DETATTN_ERR_HIP;
-  unsigned err = 0;
-  const unsigned* header = static_cast<const unsigned*>(workspace);
-  if (hipMemcpy(&err, header + 16, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess) return DETATTN_ERR_HIP;
-  if (err == kErrNone) return DETATTN_OK;
-  return (err & kErrTimeout) ? DETATTN_ERR_DEVICE_TIMEOUT : DETATTN_ERR_DEVICE_PLACEMENT;
+  // the sticky word and its tag (words kHdrSticky .. kHdrTag + 1)
+  unsigned w[4] = {0, 0, 0, 0};
+  unsigned* header = static_cast<unsigned*>(workspace);
+  if (hipMemcpy(w, header + kHdrSticky, sizeof(w), hipMemcpyDeviceToHost) != hipSuccess) return DETATTN_ERR_HIP;
+  unsigned long long tag;
+  std::memcpy(&tag, w + (kHdrTag - kHdrSticky), sizeof(tag));
+  if (tag != kStickyTag || w[0] == kErrNone) return DETATTN_OK;  // no call yet, or no error since the last read
+  const unsigned zero = 0;
+  if (hipMemcpy(header + kHdrSticky, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return DETATTN_ERR_HIP;
+  return DETATTN_ERR_DEVICE_TIMEOUT;
 }
 
 int detattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, detattn_shape_t s,

@@ -60,9 +60,6 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Round-to-nearest-even fp32 -> bf16 (v_cvt_pk_bf16_f32 on gfx950).
-__device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
-
 __device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) {
   bf16x4 r;
   r[0] = (__bf16)a;
@@ -74,14 +71,6 @@ __device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) 
 
 // Two fp32 -> two bf16 (RNE) with one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ bf16x2 cvt2(float a, float b) { return __builtin_convertvector(f32x2{a, b}, bf16x2); }
-
-// Eight accumulator registers [8h, 8h+8) of a C tile as a bf16 MFMA operand.
-__device__ __forceinline__ bf16x8 acc_slice_bf16(const f32x16& c, int h) {
-  bf16x8 r;
-#pragma unroll
-  for (int t = 0; t < 8; ++t) r[t] = (__bf16)c[8 * h + t];
-  return r;
-}
 
 // 16-byte LDS load/store.
 __device__ __forceinline__ bf16x8 lds_load16(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
@@ -148,58 +137,8 @@ __device__ __forceinline__ int swz_f(int r) {
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-// Element offset of (row r, column c) in a swizzled bf16 tile.
-template <int NCH>
-__device__ __forceinline__ int swz_off(int r, int c) {
-  return r * (NCH * 8) + ((((c >> 3) ^ swz_f<NCH>(r))) << 3) + (c & 7);
-}
-
-// frag_row on a swizzled tile: lane holds M[r0 + l%32][k0 + 8g .. +7].
-template <int NCH>
-__device__ __forceinline__ bf16x8 frag_row_s(const __bf16* M, int r0, int k0) {
-  const int l = threadIdx.x & 63;
-  return lds_load16(M + swz_off<NCH>(r0 + (l & 31), k0 + 8 * (l >> 5)));
-}
-
-// frag_tr on a swizzled tile (same meaning as frag_tr).
-template <int NCH>
-__device__ __forceinline__ bf16x8 frag_tr_s(const __bf16* M, int k0, int c0, bool perm) {
-  const int l = threadIdx.x & 63;
-  const int s = l & 15;
-  const int grp = l >> 4;
-  const int g = grp >> 1;
-  const int cbase = c0 + 16 * (grp & 1) + 4 * (s & 3);
-  int ka, kb;
-  if (perm) {
-    ka = k0 + 4 * g + (s >> 2);
-    kb = ka + 8;
-  } else {
-    ka = k0 + 8 * g + (s >> 2);
-    kb = ka + 4;
-  }
-  return cat(lds_read_tr(M + swz_off<NCH>(ka, cbase)), lds_read_tr(M + swz_off<NCH>(kb, cbase)));
-}
-
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void gbl_void;
-
-// Asynchronous global -> LDS copy of `rows` rows of NCH*8 bf16 (row-major,
-// contiguous in global memory) into a swizzled LDS tile, split over the 4
-// waves of the workgroup. Each wave instruction moves 1 KB: lane l writes the
-// 16 bytes at LDS offset 16*l of the instruction's block, so the swizzle is
-// applied by choosing which global chunk each lane fetches. Completion is
-// tracked by vmcnt.
-template <int NCH>
-__device__ __forceinline__ void dma_tile(__bf16* lds_tile, const __bf16* __restrict__ gsrc, int rows) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n_ins = rows * NCH / 64;
-  for (int ins = w; ins < n_ins; ins += 4) {
-    const int q = ins * 64 + lane;  // physical chunk index inside the tile
-    const int r = q / NCH, p = q % NCH;
-    const __bf16* src = gsrc + r * (NCH * 8) + ((p ^ swz_f<NCH>(r)) << 3);
-    __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)(lds_tile + ins * 512), 16, 0, 0);
-  }
-}
 
 // Asynchronous copy of n (a multiple of 64) fp32 values to LDS, by wave `wv`.
 __device__ __forceinline__ void dma_f32(float* lds, const float* __restrict__ gsrc, int n, int wv) {
@@ -215,9 +154,29 @@ __device__ __forceinline__ void wait_vm_all() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Workspace header (32-bit words). The preprocess kernel zeroes words
+// [0, kHdrZeroWords) at the start of every call; the sticky status and its
+// tag survive calls.
+//   kHdrTicket      dynamic item counter of the ticket dispatch
+//   kHdrAbort       error bits of the current call: a wait that sees it set
+//                   gives up at once, so a failing call drains quickly
+//   kHdrXcdCount    8 counters: workgroups that registered on each XCD
+//   kHdrXcdArrived  workgroups registered so far (the registration barrier)
+//   kHdrSticky      error bits of every call since the status was last read
+//                   (detattn_device_status reads and clears them)
+//   kHdrTag         two words: kStickyTag once the sticky word was initialised
+static constexpr int kHdrTicket = 0;
+static constexpr int kHdrAbort = 16;
+static constexpr int kHdrXcdCount = 24;
+static constexpr int kHdrXcdArrived = 32;
+static constexpr int kHdrZeroWords = 48;
+static constexpr int kHdrSticky = 48;
+static constexpr int kHdrTag = 50;
+static constexpr unsigned long long kStickyTag = 0x5354494b59444154ull;
+
 // Workspace layout (all offsets in bytes from the workspace base).
 struct WsLayout {
-  static constexpr size_t kHeader = 256;         // ticket @0, error word @64, error detail @128
+  static constexpr size_t kHeader = 256;         // the header words above
   static constexpr size_t kFlagStride = 128;     // one L2 line per dQ tile flag
   static constexpr size_t kMinBlockQ = 64;
   size_t flags_off, flags_bytes, ndelta_off, row_bytes, nlse_off, dqacc_off, dqacc_bytes, total;
@@ -235,6 +194,6 @@ struct WsLayout {
   __host__ __device__ static size_t align(size_t x) { return (x + 255) & ~(size_t)255; }
 };
 
-enum DeviceError : uint32_t { kErrNone = 0, kErrTimeout = 1, kErrPlacement = 2 };
+enum DeviceError : uint32_t { kErrNone = 0, kErrTimeout = 1 };
 
 }  // namespace detattn

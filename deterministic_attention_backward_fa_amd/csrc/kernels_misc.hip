@@ -57,7 +57,7 @@ static int grid_for(long long work_items, int per_block, int cap) {
   return (int)g;
 }
 
-hipError_t launch_pre(int D, const __bf16* o, const __bf16* dout, const float* lse, float inv_scale, float* nlse,
+hipError_t launch_pre(int D, const __bf16* o, const __bf16* dout, const float* lse, float* nlse,
                       float* ndelta,
                       long long rows, int* flags,
                       long long n_flags, unsigned* header, float* dqacc, long long dqacc_elems, hipStream_t st) {
@@ -67,9 +67,9 @@ hipError_t launch_pre(int D, const __bf16* o, const __bf16* dout, const float* l
   // the same grid also zeroes the flags and (unordered mode) the accumulator with grid-stride loops
   const long long dq4 = dqacc ? dqacc_elems / 4 : 0;
   if (D == 64)
-    bwd_pre_kernel<64><<<dim3((unsigned)g), dim3(256), 0, st>>>(o, dout, lse, inv_scale, nlse, ndelta, rows, flags, n_flags, header, dqacc, dq4);
+    bwd_pre_kernel<64><<<dim3((unsigned)g), dim3(256), 0, st>>>(o, dout, lse, nlse, ndelta, rows, flags, n_flags, header, dqacc, dq4);
   else
-    bwd_pre_kernel<128><<<dim3((unsigned)g), dim3(256), 0, st>>>(o, dout, lse, inv_scale, nlse, ndelta, rows, flags, n_flags, header,
+    bwd_pre_kernel<128><<<dim3((unsigned)g), dim3(256), 0, st>>>(o, dout, lse, nlse, ndelta, rows, flags, n_flags, header,
                                                                  dqacc, dq4);
   return hipGetLastError();
 }

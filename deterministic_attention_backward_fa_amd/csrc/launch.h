@@ -36,7 +36,7 @@ inline MainInfo main_info(int D, int BQ, int BKV, int causal, int dq_mode, bool 
   return MainInfo{nullptr, 0, 0};
 }
 
-hipError_t launch_pre(int D, const __bf16* o, const __bf16* dout, const float* lse, float inv_scale, float* nlse,
+hipError_t launch_pre(int D, const __bf16* o, const __bf16* dout, const float* lse, float* nlse,
                       float* ndelta,
                       long long rows, int* flags,
                       long long n_flags, unsigned* header, float* dqacc, long long dqacc_elems, hipStream_t st);

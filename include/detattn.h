@@ -28,7 +28,9 @@
  *  - Return value: a detattn_status_t. Argument errors return before anything
  *    is enqueued. No C++ exception crosses this interface.
  *  - Supported now: D in {64, 128}; S a multiple of 64 (and of the chosen KV
- *    tile); B*H*S*D < 2^31. B*H == 0 or S == 0 is a valid empty call.
+ *    tile); B*H*S*D < 2^31 and S*D*4 < 2^31 (one head's fp32 dQ accumulator
+ *    is addressed with 32-bit offsets), else DETATTN_ERR_INVALID_ARG. B*H == 0
+ *    or S == 0 is a valid empty call.
  */
 #ifndef DETATTN_H_
 #define DETATTN_H_
@@ -89,7 +91,7 @@ typedef enum {
   DETATTN_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
   DETATTN_ERR_HIP = 4,           /* a HIP runtime call failed (launch, copy, sync) */
   DETATTN_ERR_DEVICE_TIMEOUT = 5, /* an ordered dQ wait timed out on the device */
-  DETATTN_ERR_DEVICE_PLACEMENT = 6 /* XCD-local mode: a workgroup ran on an unexpected XCD */
+  DETATTN_ERR_DEVICE_PLACEMENT = 6 /* no longer returned: XCD-local rings now follow the hardware placement */
 } detattn_status_t;
 
 /* dQ accumulation mechanism for the ordered schedules. */
@@ -97,9 +99,10 @@ typedef enum {
   DETATTN_DQ_DEFAULT = 0,
   DETATTN_DQ_ORDERED_RMW = 1,   /* load + add + store of the fp32 accumulator, in rank order */
   DETATTN_DQ_ORDERED_ATOMIC = 2, /* fp32 atomic adds issued in rank order (same order, same bits per run) */
-  DETATTN_DQ_XCD_LOCAL_RMW = 3   /* ring schedules whose ring fits one XCD: read-modify-write and flags kept
-                                    coherent in that XCD's L2 (never leave it during the kernel); the
-                                    library checks the workgroup-to-XCD placement on the device */
+  DETATTN_DQ_XCD_LOCAL_RMW = 3   /* ring schedules whose ring fits one XCD: read-modify-write kept coherent
+                                    in that XCD's L2 (never leaves it during the kernel); each workgroup
+                                    joins a ring of the XCD the hardware reports it runs on, so the result
+                                    does not depend on how workgroups are dispatched to XCDs */
 } detattn_dq_mode_t;
 
 /*
@@ -124,7 +127,12 @@ typedef struct {
                                 tile (detattn_trace_phase_t); unused records stay as the caller left them */
   int32_t trace_records;     /* records per workgroup in `trace` */
   int32_t ring_size;         /* SHIFT / SYMMETRIC_SHIFT: workgroups per ring G, a divisor of the items per head;
-                                0 = default: the items per head if at most 32, else the largest divisor <= 32.
+                                0 = default, chosen from the shape alone (B*H and the item count) for 8 XCDs
+                                of 32 workgroups: the divisor G <= 32 whose rings of one XCD give the shortest
+                                makespan (B*H heads, items/G rounds each), larger G on ties; or, when that keeps
+                                too little of the chip busy (a prime item count above 32, say), one ring as wide
+                                as the item count, spanning XCDs. With power-of-two shapes and at least
+                                four heads this is min(items, 32).
                                 With G below the item count, workgroup g of a ring takes items g, G+g, ... in
                                 rounds, and a dQ tile's order is round-major, step order inside a round
                                 (the pages' schedules are the single round G = items per head). G sets the
@@ -134,8 +142,9 @@ typedef struct {
                                 KV tile) order, 2 = static rings like the shift schedules (ring_size applies;
                                 a ring of one XCD keeps the dQ adds in that XCD's L2: read-modify-write for
                                 the ordered schedules, fp32 atomic adds for ATOMIC_NONDET), 0 = default:
-                                SERIAL_ASCENDING / DESCENDING_Q on rings where a ring fits one XCD, else
-                                on the ticket counter; ATOMIC_NONDET on the ticket counter with
+                                SERIAL_ASCENDING / DESCENDING_Q on rings of one XCD where their estimated
+                                makespan beats the ticket counter's (which pays device-scope ordered adds),
+                                else on the ticket counter; ATOMIC_NONDET on the ticket counter with
                                 device-scope adds (measured faster than adds kept in one XCD's L2). The
                                 accumulation order of the ordered schedules, rank = KV tile, is the same
                                 in both. Ignored by SHIFT / SYMMETRIC_SHIFT (always rings). */
@@ -206,9 +215,12 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
 int detattn_bwd_plan(detattn_shape_t shape, detattn_mask_t mask, detattn_schedule_t schedule,
                      const detattn_bwd_options_t* options, detattn_plan_t* plan);
 
-/* Synchronise `stream` and read the device error word of the last call that
- * used `workspace`: DETATTN_OK, DETATTN_ERR_DEVICE_TIMEOUT or
- * DETATTN_ERR_DEVICE_PLACEMENT (or ERR_HIP). */
+/* Synchronise `stream` and read the device status word of `workspace`: the
+ * errors of every call that used it since the status was last read (the word
+ * is sticky: a later successful call does not clear it; this read does).
+ * DETATTN_OK, DETATTN_ERR_DEVICE_TIMEOUT (an ordered dQ wait, or the start-up
+ * registration of XCD-local rings, ran out of time: that call's dQ is not
+ * valid), or ERR_HIP. A workspace no call has used yet reads OK. */
 int detattn_device_status(void* workspace, void* stream);
 
 /* Static, human-readable name of a status code. */

@@ -209,8 +209,9 @@ def test_library_ring_ranks_match_oracle(sched, mask, n_kv, r):
 
 
 def test_ring_option_in_plan():
-    """Default rings: a head's items if they fit one XCD (32 workgroups), else
-    the largest divisor <= 32; an explicit ring_size must divide the items."""
+    """Default rings at these shapes: a head's items if they fit one XCD (32
+    workgroups), else 32 (items in rounds); an explicit ring_size must divide
+    the items."""
     kv64 = dict(block_q=64, block_kv=64)
     p = da.detattn_bwd_plan(1, 16, 16384, 128, True, "symmetric_shift", grid=256, **kv64)
     assert (p["n_kv"], p["ring"], p["rings"], p["grid"]) == (256, 32, 8, 256)
@@ -226,15 +227,61 @@ def test_ring_option_in_plan():
         da.detattn_bwd_plan(1, 16, 16384, 128, False, "shift", grid=256, ring_size=48, **kv64)
 
 
-@pytest.mark.parametrize("S,D,causal,grid,want", [
-    (4096, 128, False, 256, "descending_q"), (8192, 128, True, 256, "symmetric_shift"),
-    (2048, 64, True, 256, "symmetric_shift"), (16384, 128, False, 256, "descending_q"),
-    (4096, 128, False, 100, "shift"),                                # no ring fits one XCD
-    (384, 128, True, 256, "descending_q"),                           # 3 KV tiles: no symmetric pairing
-    (192, 128, True, 256, "descending_q"),                           # 64-row KV tiles (S % 128 != 0), 3 of them
+@pytest.mark.parametrize("H,S,D,causal,grid,want", [
+    (2, 4096, 128, False, 256, "descending_q"), (2, 8192, 128, True, 256, "symmetric_shift"),
+    (2, 2048, 64, True, 256, "symmetric_shift"), (16, 16384, 128, False, 256, "descending_q"),
+    (2, 4096, 128, False, 100, "shift"),                             # no ring fits one XCD
+    (2, 384, 128, True, 256, "descending_q"),                        # 3 KV tiles: no symmetric pairing
+    (2, 192, 128, True, 256, "descending_q"),                        # 64-row KV tiles (S % 128 != 0), 3 of them
+    (2, 16384, 128, False, 256, "shift"),    # two heads: rings of one XCD would keep 64 workgroups busy
 ])
-def test_auto_schedule_resolves_from_the_shape(S, D, causal, grid, want):
-    p = da.detattn_bwd_plan(1, 2, S, D, causal, "auto", grid=grid)
+def test_auto_schedule_resolves_from_the_shape(H, S, D, causal, grid, want):
+    p = da.detattn_bwd_plan(1, H, S, D, causal, "auto", grid=grid)
     assert da.SCHEDULE_NAMES[p["schedule"]] == want
-    q = da.detattn_bwd_plan(1, 2, S, D, causal, want, grid=grid)
+    q = da.detattn_bwd_plan(1, H, S, D, causal, want, grid=grid)
     assert p == q
+
+
+@pytest.mark.parametrize("H,n_kv", [(16, 37), (32, 37), (16, 40), (32, 40), (1, 64), (3, 37)])
+@pytest.mark.parametrize("sched,causal", [("serial_ascending", False), ("descending_q", False), ("shift", False),
+                                          ("serial_ascending", True), ("descending_q", True),
+                                          ("symmetric_shift", True), ("auto", False), ("auto", True)])
+def test_plans_keep_the_chip_busy_at_any_length(H, n_kv, sched, causal):
+    """Sequence lengths whose tile counts are not powers of two (a prime count
+    of 128-row KV tiles, say): whatever the divisors of the item count, the
+    default plan's makespan in item times (a ring's heads one after the other,
+    items / G rounds each; twice as long per item on a ring spanning XCDs, 1.8x
+    on the ticket counter, the measured costs of device-scope dQ adds) stays
+    within 2.5x the ideal of all items spread over 256 workgroups (ring sizes
+    must divide the item count: a prime count of 37 items per head leaves one
+    ring of 37 workgroups spanning XCDs, six at a time)."""
+    S = n_kv * 128
+    if sched == "symmetric_shift" and n_kv % 2:
+        with pytest.raises(da.DetAttnError):
+            da.detattn_bwd_plan(1, H, S, 128, causal, sched, grid=256)
+        return
+    p = da.detattn_bwd_plan(1, H, S, 128, causal, sched, grid=256)
+    items_per_head = p["items"] // H
+    ideal = -(-p["items"] // 256)
+    if p["ring"]:
+        rounds = -(-H // min(p["rings"], H)) * (items_per_head // p["ring"])
+        cost = rounds * (1.0 if p["dq_mode"] == da.DQ_MODES["xcd_local"] else 2.0)
+    else:
+        cost = -(-p["items"] // p["grid"]) * 1.8
+    assert cost <= 2.5 * ideal, p
+
+
+def test_default_ring_depends_on_the_shape_only():
+    """The shift schedules' default ring size sets the dQ order, so it must not
+    follow the grid: the same G with any grid."""
+    for causal, sched in ((False, "shift"), (True, "symmetric_shift")):
+        for H, S in ((16, 4736 * 2), (32, 5120), (1, 16384), (32, 8192)):
+            rings = {da.detattn_bwd_plan(1, H, S, 128, causal, sched, grid=g)["ring"] for g in (256, 248, 512)}
+            assert len(rings) == 1, (sched, H, S, rings)
+
+
+def test_shape_bounds_for_32_bit_offsets():
+    """One head's fp32 dQ accumulator (S*D*4 bytes) must stay below 2^31."""
+    assert _bwd_status((1, 1, (1 << 22), 128, 0.1), opts=da._options(grid=8)) == 1   # S*D*4 = 2^31
+    assert _bwd_status((1, 1, (1 << 22) - 64, 128, 0.1), opts=da._options(grid=8)) != 1
+    assert da.detattn_bwd_workspace_bytes(1, 1, 1 << 22, 128) == 0

@@ -6,9 +6,12 @@ outputs one by one on two heads (the first and the last): dQ at sampled query
 rows, dK and dV at sampled key rows, plus every row's log-sum-exp. The bar is
 the same as for the small cases, max|gpu - oracle| <= 2e-2 * max|oracle| over
 the sampled values, and the bitwise relations between schedules that share an
-accumulation order hold at full size. The long-context shapes also repeat
-every schedule 100 times and require identical bits.
+accumulation order hold at full size. Every deterministic schedule of the
+workload shapes repeats 100 times (2 at 64k tokens) with identical bits and a
+clean device status after every call; the SHA-256 of each schedule's outputs
+is printed.
 """
+import hashlib
 import math
 
 import numpy as np
@@ -25,9 +28,9 @@ pytestmark = pytest.mark.gpu
 
 CONFIGS = {
     # name: (B, H, S, D, causal, seed, runs for the determinism check, options)
-    "causal_b4_h16_s2048_d64": (4, 16, 2048, 64, True, 102, 3, {}),
-    "full_b2_h32_s4096_d128": (2, 32, 4096, 128, False, 103, 3, {}),
-    "causal_b1_h32_s8192_d128": (1, 32, 8192, 128, True, 104, 3, {}),
+    "causal_b4_h16_s2048_d64": (4, 16, 2048, 64, True, 102, 100, {}),
+    "full_b2_h32_s4096_d128": (2, 32, 4096, 128, False, 103, 100, {}),
+    "causal_b1_h32_s8192_d128": (1, 32, 8192, 128, True, 104, 100, {}),
     # the long-context workload with its stated 64-row KV tile, then with the library's default tile
     "full_b1_h16_s16384_d128_kv64": (1, 16, 16384, 128, False, 105, 100, {"block_q": 64, "block_kv": 64}),
     "causal_b1_h16_s16384_d128_kv64": (1, 16, 16384, 128, True, 105, 100, {"block_q": 64, "block_kv": 64}),
@@ -76,13 +79,18 @@ def test_fullsize_sampled_parity_and_determinism(name):
                 e = rel_err(got.float().cpu().numpy(), want)
                 assert e <= TOL, f"{name} {sched} head ({b},{h}) {label}: rel err {e:.3e}"
         if sched != "atomic_nondet":
+            digest = hashlib.sha256()
+            for t in first:
+                digest.update(t.view(torch.int16).cpu().numpy().tobytes())
+            say(f"[fullsize] {name}: {sched} sha256(dq|dk|dv) {digest.hexdigest()}")
             out = tuple(torch.empty_like(t) for t in first)
-            for _ in range(runs - 1):
+            for run in range(runs - 1):
                 da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule=sched, workspace=ws, out=out,
                                           **opts)
+                assert da.detattn_device_status(ws) == 0, f"{name} {sched} run {run + 2}: device status"
                 for a, b_ in zip(first, out):
-                    assert same_bits(a, b_), f"{name} {sched} not bit-identical across runs"
-            assert da.detattn_device_status(ws) == 0
+                    assert same_bits(a, b_), f"{name} {sched} run {run + 2} not bit-identical to run 1"
+            say(f"[fullsize] {name}: {sched} {runs} runs bit-identical")
         outs[sched] = first
     if not opts:
         # the automatic choice is the measured-fastest deterministic schedule: same plan, same bits

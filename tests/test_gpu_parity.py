@@ -166,10 +166,20 @@ def test_timeout_path_reports_and_exits(dispatch):
     say(f"[timeout path] serial_ascending ({dispatch} dispatch), item 0 withholds its first signal")
     da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=False, schedule="serial_ascending", workspace=ws,
                               debug_skip_signal=1, timeout_us=2000, dispatch=dispatch)
-    assert da.detattn_device_status(ws) == 5
-    # the next normal call on the same workspace is clean again
+    # the status is sticky: a later successful call on the workspace does not hide the failure
     da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=False, schedule="serial_ascending", workspace=ws,
                               dispatch=dispatch)
+    assert da.detattn_device_status(ws) == 5
+    # reading the status clears it; a normal call leaves it clean
+    assert da.detattn_device_status(ws) == 0
+    da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=False, schedule="serial_ascending", workspace=ws,
+                              dispatch=dispatch)
+    assert da.detattn_device_status(ws) == 0
+    # the binding's check raises on the failing call itself
+    say(f"[timeout path] check=True raises")
+    with pytest.raises(da.DetAttnError):
+        da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=False, schedule="serial_ascending", workspace=ws,
+                                  debug_skip_signal=1, timeout_us=2000, dispatch=dispatch, check=True)
     assert da.detattn_device_status(ws) == 0
 
 
@@ -243,3 +253,49 @@ def test_gradient_identities_on_gpu_output(case):
         assert torch.all(sk <= 1e-2 * dk64.abs().sum(dim=2) + 1e-6), sched
         sv = (dv64.sum(dim=2) - do64.sum(dim=2)).abs()
         assert torch.all(sv <= 1e-2 * dv64.abs().sum(dim=2) + 1e-6), sched
+
+
+TRACE_CASES = [
+    # (B, H, S, D, causal, seed, options): two small shapes per mask, both head dimensions
+    (1, 2, 512, 64, False, 31, {}),
+    (1, 2, 512, 128, False, 32, {}),
+    (1, 2, 512, 64, True, 33, {}),
+    (1, 2, 1024, 128, True, 34, {}),
+]
+
+
+@pytest.mark.parametrize("case", TRACE_CASES, ids=lambda c: f"B{c[0]}H{c[1]}S{c[2]}D{c[3]}{'c' if c[4] else 'f'}")
+def test_traced_instances_match_oracle_and_untraced_bits(case):
+    """The phase-traced kernel instances (their own translation units) compute
+    the same thing: oracle parity at the same bar, and every output bit-equal to
+    the untraced instance of the same plan; the trace records are well formed."""
+    B, H, S, D, causal, seed, opts = case
+    scale = 1.0 / math.sqrt(D)
+    cpu, (q, k, v, do, o, lse) = inputs(B, H, S, D, seed, causal)
+    dq_r, dk_r, dv_r, _, _ = _oracle(cpu, causal, scale)
+    for sched in schedules_for(causal):
+        if sched == "atomic_nondet":
+            continue
+        plan = da.detattn_bwd_plan(B, H, S, D, causal, sched, **opts)
+        recs = 64
+        trace = torch.zeros(plan["grid"] * recs * 2, dtype=torch.int64, device="cuda")
+        ws = da.alloc_workspace(B, H, S, D)
+        say(f"[traced] {case[:5]} {sched} plan {plan}")
+        base = [t.clone() for t in da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule=sched,
+                                                            workspace=ws, **opts)]
+        got = da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule=sched, workspace=ws,
+                                        trace=trace, trace_records=recs, **opts)
+        assert da.detattn_device_status(ws) == 0
+        for name, g, want in (("dq", got[0], dq_r), ("dk", got[1], dk_r), ("dv", got[2], dv_r)):
+            e = rel_err(g.float().cpu().numpy(), want)
+            assert e <= TOL, f"traced {sched} {name} rel err {e:.3e}"
+        assert all(same_bits(a, b) for a, b in zip(base, got)), f"traced {sched} differs from untraced"
+        t = trace.view(plan["grid"], recs, 2).cpu()
+        used = t[:, :, 0] != 0
+        assert used.any()
+        phases = (t[:, :, 1] & 0xFF)[used]
+        assert int(phases.max()) <= 7
+        # timestamps never decrease within a workgroup's records
+        for w in range(plan["grid"]):
+            ts = t[w, :, 0][used[w]]
+            assert torch.all(ts[1:] >= ts[:-1]), (sched, w)
