@@ -324,7 +324,7 @@ def main():
         line["trace_share"] = {k: round(v, 4) for k, v in summ["share"].items()}
         if args.trace_gantt:
             log(f"[bench] timeline of {headline} ('#' tile compute, 'w' waiting for the dQ turn, "
-                f"'e' column switch, ' ' idle; one row per workgroup):")
+                f"'e' column switch, 's' start-up (registration, first K/V), ' ' idle; one row per workgroup):")
             log(dtrace.gantt(recs))
     # The metric covers both masks: the default run also times the full-mask
     # workload (every schedule) and reports it beside the causal headline.

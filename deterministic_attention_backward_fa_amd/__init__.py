@@ -205,6 +205,7 @@ def attn_bwd_deterministic(q, k, v, o, dout, lse, causal=False, schedule="serial
 
 
 def detattn_device_status(workspace, stream=None) -> int:
+    """Status word of `workspace` (sticky: the errors of every call since the last read)."""
     return int(lib().detattn_device_status(_ptr(workspace), _stream(stream)))
 
 

@@ -47,7 +47,8 @@ struct BwdArgs {
   unsigned* ticket;    // dynamic item counter
   unsigned* err;       // error bits of this call (workspace header, kHdrAbort)
   unsigned* sticky;    // error bits kept until the status is read (kHdrSticky)
-  unsigned* xcd_reg;   // XCD registration: 8 per-XCD counters, then the arrival count
+  unsigned* xcd_tab;   // XCD registration: per workgroup, 1 + the XCD it runs on
+  unsigned* xcd_arrived;  // XCD registration: workgroups registered so far
   int BH, S;
   float scale;
   Sched sc;

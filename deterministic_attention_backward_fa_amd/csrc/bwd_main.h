@@ -162,7 +162,7 @@ struct MainCfg {
   static constexpr int OUT_BYTES = BKV * PO * 2;
   static constexpr int EPI_END = RED_BYTES + OUT_BYTES;
   static constexpr int OFF_MISC = TILE_END > EPI_END ? TILE_END : EPI_END;
-  static constexpr int LDS_BYTES = OFF_MISC + 16;
+  static constexpr int LDS_BYTES = OFF_MISC + 64;  // 16 ints: ticket, XCD registration
   static_assert(NKVW * NQW == 4, "4 waves");
   static_assert(QW % 32 == 0 && MQD >= 1 && DGRP * DW == ND && 4 * DW * MQD == ND * (BQ / 32), "tile shape");
   static_assert(MQD == 1, "one dS row block per wave (the swizzled dS reads use per-lane offsets)");
@@ -560,60 +560,45 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
   for (int x = 0; x < C::DMA_QW; ++x) goffQ[x] = dma_goff<C::NCH>(w + 4 * x, lane);
 
+  // Optional phase trace: wave 0, lane 0 of each workgroup.
+  int trace_n = 0;
+  auto trace_at = [&](int phase, int t, long long item, unsigned long long when) {
+    if constexpr (TRACE) {
+      if (tid == 0 && trace_n < a.trace_records) {
+        unsigned long long* p = a.trace + ((size_t)blockIdx.x * a.trace_records + trace_n) * 2;
+        p[0] = when;
+        p[1] = (unsigned long long)phase | ((unsigned long long)(t & 0xFFFFFF) << 8) | ((unsigned long long)item << 32);
+        ++trace_n;
+      }
+    }
+  };
+  auto trace_rec = [&](int phase, int t, long long item) {
+    if constexpr (TRACE) trace_at(phase, t, item, __builtin_amdgcn_s_memtime());
+  };
+  // the workgroup's start, recorded once the ring set-up is done
+  const unsigned long long t_start = TRACE ? __builtin_amdgcn_s_memtime() : 0ull;
+
+  // Ring membership. Workgroup w is placed by a static map that assumes it
+  // runs on XCD w % 8 (ring (u / G) * 8 + w % 8, slot u % G, u = w / 8): the
+  // hardware's round-robin dispatch, which keeps each ring on one XCD.
+  // In the XCD-local dQ modes (read-modify-write and atomics kept in one XCD's
+  // L2) correctness needs that placement, so there every workgroup also
+  // registers the XCD the hardware reports (a table entry per workgroup and
+  // an arrival count, the grid being co-resident: cooperative launch), starts
+  // loading its first item under the static map, and before the item's first
+  // tile checks the registered placement: rings are formed per XCD from its
+  // registered workgroups in index order (floor(count / G) rings per XCD,
+  // numbered round-major over the XCDs), which under round-robin dispatch is
+  // the static map. Only if the two differ does the workgroup drop what it
+  // loaded and start over with the registered ring, so the result never
+  // depends on how workgroups were dispatched, and the registration wait
+  // overlaps the first K/V load.
   int ring_id = 0, slot = 0, n_rings = a.rings;
+  bool confirm = false;  // the registered placement is still to be checked
+  unsigned my_xcc = 0;
   if (!a.ticket_mode) {
     const int wg = blockIdx.x;
-    if (kLocal && a.xcd_remap) {
-      // Rings of one XCD (their dQ hand-offs stay in that XCD's L2): a
-      // workgroup joins a ring of the XCD it runs on, read from the hardware,
-      // so the mode's correctness does not rest on how workgroups are
-      // dispatched to XCDs. Every workgroup registers (the grid is
-      // co-resident: cooperative launch), then each XCD forms
-      // floor(count / G) rings from its registered workgroups in arrival
-      // order; rings are numbered round-major over the XCDs (with equal counts,
-      // ring k*8 + x is the k-th ring of XCD x). Surplus workgroups exit.
-      if (tid == 0) {
-        unsigned xcc;
-        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-        xcc &= 7;
-        const int my = (int)__hip_atomic_fetch_add(a.xcd_reg + xcc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_add(a.xcd_reg + 8, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        int rid = -1, sl = 0, nr = 0;
-        const long long t0 = now_ticks();
-        bool all = true;
-        while (__hip_atomic_load(a.xcd_reg + 8, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < gridDim.x) {
-          __builtin_amdgcn_s_sleep(1);
-          if (now_ticks() - t0 > a.timeout_ticks ||
-              __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
-            report_error(a, kErrTimeout);
-            all = false;
-            break;
-          }
-        }
-        if (all) {
-          int rx[8];
-#pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            rx[x] = (int)__hip_atomic_load(a.xcd_reg + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) / a.ring;
-            nr += rx[x];
-          }
-          const int k = my / a.ring;
-          sl = my % a.ring;
-          if (k < rx[xcc]) {
-            rid = 0;
-#pragma unroll
-            for (int x = 0; x < 8; ++x) rid += (rx[x] < k ? rx[x] : k) + ((x < (int)xcc && rx[x] > k) ? 1 : 0);
-          }
-        }
-        sMisc[1] = rid;
-        sMisc[2] = sl;
-        sMisc[3] = nr;
-      }
-      __syncthreads();
-      ring_id = __builtin_amdgcn_readfirstlane(sMisc[1]);
-      slot = __builtin_amdgcn_readfirstlane(sMisc[2]);
-      n_rings = __builtin_amdgcn_readfirstlane(sMisc[3]);
-    } else if (a.xcd_remap) {
+    if (a.xcd_remap) {
       const int x = wg & 7, u = wg >> 3;
       ring_id = (u / a.ring) * 8 + x;
       slot = u % a.ring;
@@ -621,8 +606,80 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       ring_id = wg / a.ring;
       slot = wg % a.ring;
     }
-    if (ring_id < 0 || ring_id >= n_rings) return;
+    if (kLocal && a.xcd_remap) {
+      asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(my_xcc));
+      my_xcc &= 7;
+      if (tid == 0) {
+        // relaxed device-scope atomics (no cache writeback or invalidate): the
+        // arrival increment waits, through a register dependency, for the
+        // table write to have been performed
+        const unsigned old = __hip_atomic_exchange(a.xcd_tab + wg, my_xcc + 1, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+        unsigned zero;
+        asm volatile("v_mov_b32 %0, 0 ; after %1" : "=v"(zero) : "v"(old));
+        __hip_atomic_fetch_add(a.xcd_arrived, 1u + zero, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      confirm = true;
+    } else if (ring_id >= n_rings) {
+      return;
+    }
   }
+  if (!confirm) trace_at(8, 0, 0, t_start);
+
+  // The registered placement of this workgroup (XCD-local modes; every thread
+  // takes part): waits until every workgroup has registered (bounded), then
+  // sets ring_id, slot (ring_id = -1: no ring, or the wait timed out) and
+  // n_rings from the table; returns whether they equal the static map's.
+  auto registered_ring = [&]() -> bool {
+    int* sCnt = sMisc + 4;  // 8 per-XCD counts, then this workgroup's rank on its XCD
+    if (tid < 9) sCnt[tid] = 0;
+    if (tid == 0) {
+      const long long t0 = now_ticks();
+      int ok = 1;
+      while (__hip_atomic_load(a.xcd_arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gridDim.x) {
+        __builtin_amdgcn_s_sleep(1);
+        if (now_ticks() - t0 > a.timeout_ticks ||
+            __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+          report_error(a, kErrTimeout);
+          ok = 0;
+          break;
+        }
+      }
+      sMisc[1] = ok;
+    }
+    __syncthreads();
+    const bool ok = __builtin_amdgcn_readfirstlane(sMisc[1]) != 0;
+    if (ok) {
+      for (int w2 = tid; w2 < (int)gridDim.x; w2 += kThreads) {
+        const int x2 = (int)__hip_atomic_load(a.xcd_tab + w2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - 1;
+        if (x2 >= 0 && x2 < 8) {
+          atomicAdd(sCnt + x2, 1);
+          if (x2 == (int)my_xcc && w2 < (int)blockIdx.x) atomicAdd(sCnt + 8, 1);
+        }
+      }
+    }
+    __syncthreads();
+    const int prev_ring = ring_id, prev_slot = slot, prev_n = n_rings;
+    ring_id = -1;
+    n_rings = 0;
+    if (ok) {
+      const int rank = __builtin_amdgcn_readfirstlane(sCnt[8]);
+      const int k = rank / a.ring;
+      int rid = 0;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int rx = __builtin_amdgcn_readfirstlane(sCnt[x]) / a.ring;
+        n_rings += rx;
+        rid += (rx < k ? rx : k) + ((x < (int)my_xcc && rx > k) ? 1 : 0);
+      }
+      slot = rank % a.ring;
+      if (k < __builtin_amdgcn_readfirstlane(sCnt[my_xcc]) / a.ring) ring_id = rid;
+    }
+    __syncthreads();  // the counts are read before anyone reuses them
+    trace_at(8, 0, 0, t_start);
+    trace_rec(9, slot, ring_id);  // registered: ring and slot known
+    return ring_id == prev_ring && slot == prev_slot && n_rings == prev_n;
+  };
 
   const uint32_t lbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)smem;
   const uint32_t aS = lbase + oS, aS_hi = lbase + oS_hi;
@@ -647,19 +704,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     dma_f32(ld + BQ, a.ndelta + bhS + qrow0, BQ, 1);
   };
 
-  // Optional phase trace: wave 0, lane 0 of each workgroup.
-  int trace_n = 0;
-  auto trace_rec = [&](int phase, int t, long long item) {
-    if constexpr (TRACE) {
-      if (tid == 0 && trace_n < a.trace_records) {
-        unsigned long long* p = a.trace + ((size_t)blockIdx.x * a.trace_records + trace_n) * 2;
-        p[0] = __builtin_amdgcn_s_memtime();
-        p[1] = (unsigned long long)phase | ((unsigned long long)(t & 0xFFFFFF) << 8) | ((unsigned long long)item << 32);
-        ++trace_n;
-      }
-    }
-  };
-
   // Ring mode: the ring takes heads ring_id, ring_id + rings, ...; inside a
   // head, workgroup `slot` takes one item per round of G = a.ring items: item
   // kG + slot in round k.
@@ -669,15 +713,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   int ring_bh = ring_id, ring_k0 = 0;
   bool ring_rev = false;
   for (;;) {
-    long long gidx;
+    long long gidx = -1;  // no item left
     if (a.ticket_mode) {
       if (tid == 0) sMisc[0] = (int)atomicAdd(a.ticket, 1u);
       __syncthreads();
       gidx = __builtin_amdgcn_readfirstlane(sMisc[0]);
       __syncthreads();
       if (gidx >= total_items) return;
-    } else {
-      if (ring_bh >= a.BH) return;
+    } else if (ring_id >= 0 && ring_id < n_rings && ring_bh < a.BH) {
       gidx = (long long)ring_bh * ipH + ring_k0 + (ring_rev ? a.ring - 1 - slot : slot);
       ring_k0 += a.ring;
       ring_rev = a.snake && !ring_rev;
@@ -687,8 +730,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
         ring_bh += n_rings;
       }
     }
-    const int bh = (int)(gidx / ipH);
-    const int it = (int)(gidx % ipH);
+    const int bh = gidx < 0 ? 0 : (int)(gidx / ipH);
+    const int it = gidx < 0 ? 0 : (int)(gidx % ipH);
     const long long head_off = (long long)bh * a.S * D;
     const long long bhS = (long long)bh * a.S;
     // the head's dQ accumulator as a buffer resource (32-bit offsets, range-checked)
@@ -710,6 +753,32 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     // (the epilogue's LDS staging lies below the K, V tiles).
     static_assert(C::EPI_END <= C::OFF_K, "epilogue LDS overlaps the K/V tiles");
 
+    // XCD-local rings: the registered placement is checked once, with the first
+    // item's K, V and first Q tile already on their way
+    bool first_loaded = false;
+    if (confirm) {
+      confirm = false;
+      if (gidx >= 0) {
+        int j0;
+        const SegWalk w0 = sc.walk(it, 0, j0);
+        dma_kv(head_off, j0);
+        dma_q(0, head_off, bhS, w0.i);
+      }
+      if (!registered_ring()) {
+        // placed otherwise than the static map assumed: drop what was loaded, take the registered ring
+        if (gidx >= 0) {
+          wait_vm_all();
+          __syncthreads();
+        }
+        ring_bh = ring_id;
+        ring_k0 = 0;
+        ring_rev = false;
+        continue;
+      }
+      first_loaded = gidx >= 0;
+    }
+    if (gidx < 0) return;
+
     for (int seg = 0; seg < sc.segments(); ++seg) {
     const int t_begin = sc.seg_begin(it, seg), t_end = sc.seg_end(it, seg);
     int j;
@@ -717,8 +786,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     const int i0 = cur.i;
     // ---- segment prologue: K_j, V_j (the second column of a symmetric pair has
     // them on their way already) and the first Q tile ----
-    if (seg == 0) dma_kv(head_off, j);
-    dma_q(0, head_off, bhS, i0);
+    if (!first_loaded) {
+      if (seg == 0) dma_kv(head_off, j);
+      dma_q(0, head_off, bhS, i0);
+    }
+    first_loaded = false;
     wait_vm_all();
     __syncthreads();
     // K_j, V_j (MFMA B operands of S, dP) and K_j transposed (B operand of the
@@ -833,7 +905,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       const int vL = oL + vb;
       const uint32_t aA = lbase + oA + vb, aT = lbase + oT + vb;
 
-      // ---- accumulator initial values: -LSE/scale (S), -D (dP); mask on diagonal tiles ----
+      // ---- accumulator initial values: -LSE*log2(e) (S), -D (dP); mask on diagonal tiles ----
       f32x16 sAcc[C::MQ], pAcc[C::MQ];
 #pragma unroll
       for (int m = 0; m < C::MQ; ++m)
@@ -1156,7 +1228,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       static_for<0, NB>([&](auto kc) {
         constexpr int k = decltype(kc)::value;
         if constexpr (k == kDecide && !kUnordered) {
-          early = rk == 0 || (a.delay_seed == 0 && __builtin_amdgcn_readfirstlane(seen) >= turn_val);
+          // the flag value is read on every path (also by the first contributor,
+          // which does not need it): a load whose result is never used would
+          // make the compiler wait for every vector-memory operation before
+          // the next write of its register (the next tile's row terms)
+          const int seen_u = __builtin_amdgcn_readfirstlane(seen);
+          early = rk == 0 || (a.delay_seed == 0 && seen_u >= turn_val);
           // early: the turn has come, the accumulator is read under the dQ MFMAs
           // (local mode drops stale L1 lines first); otherwise it is read after
           // waiting for the turn

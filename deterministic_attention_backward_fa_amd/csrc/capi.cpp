@@ -175,7 +175,7 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
   int ring_pref = o.ring_size;
   if (sch == DETATTN_SERIAL_ASCENDING || sch == DETATTN_DESCENDING_Q || sch == DETATTN_ATOMIC_NONDET) {
     // rank = KV tile whatever the dispatch: the ring size may follow the grid
-    const bool local_fits = xcd && grid % kXcds == 0 && grid >= kXcds;
+    const bool local_fits = xcd && grid % kXcds == 0 && grid >= kXcds && grid <= (int)WsLayout::kMaxXcdGrid;
     if (!ring_pref) {
       ring_pref = 1;
       double best = 1e301;
@@ -212,7 +212,7 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
     if (ip % sc.G != 0) return DETATTN_ERR_UNSUPPORTED;
     ring = sc.G;
     if (grid < ring) return DETATTN_ERR_UNSUPPORTED;
-    if (xcd && grid % 8 == 0 && ring <= grid / 8) {
+    if (xcd && grid % 8 == 0 && ring <= grid / 8 && grid <= (int)WsLayout::kMaxXcdGrid) {
       long long per_xcd = (grid / 8) / ring;
       const long long need = (BH + 7) / 8;
       if (per_xcd > need) per_xcd = need;
@@ -350,8 +350,8 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
   a.ticket = header + kHdrTicket;
   a.err = header + kHdrAbort;
   a.sticky = header + kHdrSticky;
-  a.xcd_reg = header + kHdrXcdCount;
-  static_assert(kHdrXcdArrived == kHdrXcdCount + 8, "registration words");
+  a.xcd_tab = reinterpret_cast<unsigned*>(ws + L.xcdtab_off);
+  a.xcd_arrived = header + kHdrXcdArrived;
   a.BH = (int)BH;
   a.S = s.S;
   a.scale = s.softmax_scale;

@@ -160,14 +160,13 @@ __device__ __forceinline__ void wait_vm_all() {
 //   kHdrTicket      dynamic item counter of the ticket dispatch
 //   kHdrAbort       error bits of the current call: a wait that sees it set
 //                   gives up at once, so a failing call drains quickly
-//   kHdrXcdCount    8 counters: workgroups that registered on each XCD
-//   kHdrXcdArrived  workgroups registered so far (the registration barrier)
+//   kHdrXcdArrived  workgroups that registered their XCD so far (XCD-local
+//                   rings; the table of registered XCDs follows the header)
 //   kHdrSticky      error bits of every call since the status was last read
 //                   (detattn_device_status reads and clears them)
 //   kHdrTag         two words: kStickyTag once the sticky word was initialised
 static constexpr int kHdrTicket = 0;
 static constexpr int kHdrAbort = 16;
-static constexpr int kHdrXcdCount = 24;
 static constexpr int kHdrXcdArrived = 32;
 static constexpr int kHdrZeroWords = 48;
 static constexpr int kHdrSticky = 48;
@@ -177,11 +176,14 @@ static constexpr unsigned long long kStickyTag = 0x5354494b59444154ull;
 // Workspace layout (all offsets in bytes from the workspace base).
 struct WsLayout {
   static constexpr size_t kHeader = 256;         // the header words above
+  static constexpr size_t kMaxXcdGrid = 1024;    // workgroups the XCD registration table holds
+  static constexpr size_t kXcdTab = kMaxXcdGrid * 4;
   static constexpr size_t kFlagStride = 128;     // one L2 line per dQ tile flag
   static constexpr size_t kMinBlockQ = 64;
-  size_t flags_off, flags_bytes, ndelta_off, row_bytes, nlse_off, dqacc_off, dqacc_bytes, total;
+  size_t xcdtab_off, flags_off, flags_bytes, ndelta_off, row_bytes, nlse_off, dqacc_off, dqacc_bytes, total;
   __host__ __device__ WsLayout(long long BH, long long S, long long D) {
-    flags_off = kHeader;
+    xcdtab_off = kHeader;
+    flags_off = kHeader + kXcdTab;
     long long nq_max = (S + (long long)kMinBlockQ - 1) / (long long)kMinBlockQ;
     flags_bytes = (size_t)(BH * nq_max) * kFlagStride;
     ndelta_off = align(flags_off + flags_bytes);  // -D per row

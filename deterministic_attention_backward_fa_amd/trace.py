@@ -11,7 +11,7 @@ import numpy as np
 import torch
 
 PHASES = {0: "tile_top", 1: "ds_ready", 2: "dq_done", 3: "turn", 4: "adds_issued", 5: "tile_end", 6: "seg_begin",
-          7: "seg_end"}
+          7: "seg_end", 8: "wg_start", 9: "registered"}
 # consecutive phase pairs inside one tile, and the name of the interval. A
 # tile whose turn had already come at its top reads the accumulator right
 # after the dS^T barrier (phase 3 before phase 2); the others wait after the
@@ -84,8 +84,8 @@ def summarize(recs):
 
 
 # Gantt symbols per interval (phase a -> phase b); the rest is compute ('#')
-_GANTT = {(2, 3): "w", (5, 7): "e", (7, 6): "e", (6, 0): "e"}
-_PRIORITY = {" ": 0, "#": 1, "e": 2, "w": 3}
+_GANTT = {(2, 3): "w", (5, 7): "e", (7, 6): "e", (6, 0): "e", (8, 9): "s", (9, 6): "s", (8, 6): "s"}
+_PRIORITY = {" ": 0, "#": 1, "e": 2, "s": 2, "w": 3}
 
 
 def gantt(recs, width=100, max_rows=64):

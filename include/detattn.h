@@ -159,7 +159,9 @@ typedef enum {
   DETATTN_TRACE_ADDS_ISSUED = 4, /* accumulator adds issued */
   DETATTN_TRACE_TILE_END = 5,    /* dV/dK products issued */
   DETATTN_TRACE_SEG_BEGIN = 6,   /* a KV column starts (K, V staged) */
-  DETATTN_TRACE_SEG_END = 7      /* its dK, dV stored */
+  DETATTN_TRACE_SEG_END = 7,     /* its dK, dV stored */
+  DETATTN_TRACE_WG_START = 8,    /* the workgroup starts (tile field 0) */
+  DETATTN_TRACE_REGISTERED = 9   /* XCD-local rings: registration done (tile field = slot, item field = ring) */
 } detattn_trace_phase_t;
 
 /* What the library chose for a call (see detattn_bwd_plan). */
