@@ -20,7 +20,8 @@ SCHEDULE_NAMES = {v: k for k, v in SCHEDULES.items()}
 DQ_MODES = {"default": 0, "rmw": 1, "atomic": 2, "xcd_local": 3}
 DISPATCH = {"default": 0, "ticket": 1, "ring": 2}
 STATUS = {0: "OK", 1: "ERR_INVALID_ARG", 2: "ERR_UNSUPPORTED", 3: "ERR_WORKSPACE", 4: "ERR_HIP",
-          5: "ERR_DEVICE_TIMEOUT", 6: "ERR_DEVICE_PLACEMENT (not returned any more)"}
+          5: "ERR_DEVICE_TIMEOUT", 6: "ERR_DEVICE_PLACEMENT (not returned any more)", 7: "ERR_SCRATCH_LIMIT"}
+NOALLOC_SCRATCH_BYTES = 136 << 20  # DETATTN_NOALLOC_SCRATCH_BYTES
 
 
 class DetAttnError(RuntimeError):
@@ -72,6 +73,8 @@ def lib():
         L.attn_bwd_deterministic.restype = ctypes.c_int
         L.attn_bwd_deterministic_ex.argtypes = bwd_args + [ctypes.POINTER(BwdOptions), vp]
         L.attn_bwd_deterministic_ex.restype = ctypes.c_int
+        L.attn_bwd_deterministic_noalloc.argtypes = [vp] * 9 + [Shape, ctypes.c_int, ctypes.c_int, vp]
+        L.attn_bwd_deterministic_noalloc.restype = ctypes.c_int
         L.detattn_bwd_plan.argtypes = [Shape, ctypes.c_int, ctypes.c_int, ctypes.POINTER(BwdOptions),
                                        ctypes.POINTER(Plan)]
         L.detattn_bwd_plan.restype = ctypes.c_int
@@ -204,8 +207,31 @@ def attn_bwd_deterministic(q, k, v, o, dout, lse, causal=False, schedule="serial
     return dq, dk, dv
 
 
+def attn_bwd_deterministic_noalloc(q, k, v, o, dout, lse, causal=False, schedule="serial_ascending", scale=None,
+                                   out=None, stream=None):
+    """attn_bwd_deterministic on the library's fixed per-GPU scratch (no workspace;
+    the C entry point allocates nothing). `out` = (dq, dk, dv) is allocated here
+    only when not given."""
+    B, H, S, D = q.shape
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_tensor(n, t, torch.bfloat16, (B, H, S, D))
+    _check_tensor("lse", lse, torch.float32, (B, H, S))
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = out
+    for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_tensor(n, t, torch.bfloat16, (B, H, S, D))
+    st = lib().attn_bwd_deterministic_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                                              _ptr(dk), _ptr(dv), _shape(q, scale),
+                                              MASKS["causal" if causal else "full"], SCHEDULES[schedule],
+                                              _stream(stream))
+    if st != 0:
+        raise DetAttnError(st, f"attn_bwd_deterministic_noalloc({schedule})")
+    return dq, dk, dv
+
+
 def detattn_device_status(workspace, stream=None) -> int:
-    """Status word of `workspace` (sticky: the errors of every call since the last read)."""
+    """Status word of `workspace` (None: the no-alloc scratch of the current device)."""
     return int(lib().detattn_device_status(_ptr(workspace), _stream(stream)))
 
 

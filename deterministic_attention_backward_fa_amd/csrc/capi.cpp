@@ -13,6 +13,10 @@
 
 using namespace detattn;
 
+namespace detattn {
+void* noalloc_scratch_if_ready();  // noalloc.hip
+}
+
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -277,6 +281,7 @@ const char* detattn_status_string(int status) {
     case DETATTN_ERR_HIP: return "HIP runtime error";
     case DETATTN_ERR_DEVICE_TIMEOUT: return "ordered dQ wait timed out on the device";
     case DETATTN_ERR_DEVICE_PLACEMENT: return "a workgroup ran on an unexpected XCD (no longer reported)";
+    case DETATTN_ERR_SCRATCH_LIMIT: return "shape needs more workspace than the no-alloc scratch holds";
     default: return "unknown status";
   }
 }
@@ -402,6 +407,7 @@ int attn_bwd_deterministic(const void* q, const void* k, const void* v, const vo
 }
 
 int detattn_device_status(void* workspace, void* stream) {
+  if (!workspace) workspace = noalloc_scratch_if_ready();
   if (!workspace) return DETATTN_ERR_INVALID_ARG;
   if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return DETATTN_ERR_HIP;
   // the sticky word and its tag (words kHdrSticky .. kHdrTag + 1)

@@ -91,7 +91,9 @@ typedef enum {
   DETATTN_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
   DETATTN_ERR_HIP = 4,           /* a HIP runtime call failed (launch, copy, sync) */
   DETATTN_ERR_DEVICE_TIMEOUT = 5, /* an ordered dQ wait timed out on the device */
-  DETATTN_ERR_DEVICE_PLACEMENT = 6 /* no longer returned: XCD-local rings now follow the hardware placement */
+  DETATTN_ERR_DEVICE_PLACEMENT = 6, /* no longer returned: XCD-local rings now follow the hardware placement */
+  DETATTN_ERR_SCRATCH_LIMIT = 7     /* attn_bwd_deterministic_noalloc: the shape needs more workspace than its
+                                       fixed scratch (DETATTN_NOALLOC_SCRATCH_BYTES) holds */
 } detattn_status_t;
 
 /* dQ accumulation mechanism for the ordered schedules. */
@@ -212,12 +214,38 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
                               size_t workspace_bytes, detattn_shape_t shape, detattn_mask_t mask,
                               detattn_schedule_t schedule, const detattn_bwd_options_t* options, void* stream);
 
+/*
+ * attn_bwd_deterministic without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The workspace is a fixed array in the
+ * library's device code, one per GPU, of DETATTN_NOALLOC_SCRATCH_BYTES
+ * (136 MiB: every shape with B*H*S*D <= 2^25 at D = 128 or 64, the 8k- and
+ * 16k-token workloads included); each GPU the entry point runs on holds it until
+ * the process ends. The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); its first call on a device looks the array's
+ * device address up (hipGetSymbolAddress) with that device current.
+ *  - Arguments, results and bits as attn_bwd_deterministic with default options.
+ *  - A shape whose workspace (detattn_bwd_workspace_bytes) exceeds the scratch
+ *    returns DETATTN_ERR_SCRATCH_LIMIT before any HIP call.
+ *  - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *    call's contents (each call clears what must start at zero). Calls that
+ *    overlap on one GPU (two streams, two threads) race: serialise them.
+ *  - detattn_device_status(NULL, stream) reads the scratch's status word on the
+ *    current device.
+ */
+#define DETATTN_NOALLOC_SCRATCH_BYTES (136ull << 20)
+int attn_bwd_deterministic_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                   const float* lse, void* dq, void* dk, void* dv, detattn_shape_t shape,
+                                   detattn_mask_t mask, detattn_schedule_t schedule, void* stream);
+
 /* Resolve tiles, grid and rings for a call without launching anything.
  * Needs a HIP device for the compute-unit count unless options->grid > 0. */
 int detattn_bwd_plan(detattn_shape_t shape, detattn_mask_t mask, detattn_schedule_t schedule,
                      const detattn_bwd_options_t* options, detattn_plan_t* plan);
 
-/* Synchronise `stream` and read the device status word of `workspace`: the
+/* Synchronise `stream` and read the device status word of `workspace` (NULL:
+ * the no-alloc scratch of the current device, once attn_bwd_deterministic_noalloc
+ * has run there; before that NULL is DETATTN_ERR_INVALID_ARG): the
  * errors of every call that used it since the status was last read (the word
  * is sticky: a later successful call does not clear it; this read does).
  * DETATTN_OK, DETATTN_ERR_DEVICE_TIMEOUT (an ordered dQ wait, or the start-up

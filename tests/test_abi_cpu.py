@@ -33,7 +33,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(7):
+    for code in range(8):
         assert da.status_string(code) and da.status_string(code) != "unknown status"
     assert da.status_string(99) == "unknown status"
 
@@ -285,3 +285,19 @@ def test_shape_bounds_for_32_bit_offsets():
     assert _bwd_status((1, 1, (1 << 22), 128, 0.1), opts=da._options(grid=8)) == 1   # S*D*4 = 2^31
     assert _bwd_status((1, 1, (1 << 22) - 64, 128, 0.1), opts=da._options(grid=8)) != 1
     assert da.detattn_bwd_workspace_bytes(1, 1, 1 << 22, 128) == 0
+
+
+def test_noalloc_entry_refuses_before_any_hip_call():
+    """attn_bwd_deterministic_noalloc checks the shape against its fixed scratch
+    first: too large a shape is DETATTN_ERR_SCRATCH_LIMIT, an invalid one
+    INVALID_ARG, with no device in reach; the no-alloc status needs a device
+    that has run the entry point."""
+    L = da.lib()
+    p = ctypes.c_void_p(0x10000)
+    assert L.attn_bwd_deterministic_noalloc(p, p, p, p, p, p, p, p, p, da.Shape(1, 64, 8192, 128, 0.088), 1, 3,
+                                            None) == 7
+    assert L.attn_bwd_deterministic_noalloc(p, p, p, p, p, p, p, p, p, da.Shape(1, -1, 8192, 128, 0.088), 1, 3,
+                                            None) == 1
+    # the largest workload shapes here fit: B*H*S*D = 2^25
+    assert da.detattn_bwd_workspace_bytes(1, 32, 8192, 128) <= da.NOALLOC_SCRATCH_BYTES
+    assert da.detattn_bwd_workspace_bytes(4, 16, 8192, 64) <= da.NOALLOC_SCRATCH_BYTES
