@@ -208,6 +208,8 @@ def main():
                     help="with --trace: also print a text timeline of the traced workgroups")
     ap.add_argument("--no-companion", action="store_true",
                     help="skip the full-mask companion workload of the default run")
+    ap.add_argument("--xcd-study", action="store_true",
+                    help="only measure the device-scope flag hand-off between workgroup pairs on one XCD and across XCDs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -229,6 +231,22 @@ def main():
 
     import deterministic_attention_backward_fa_amd as da
     from deterministic_attention_backward_fa_amd.synth import make_qkvdo
+
+    if args.xcd_study:
+        # workgroups w and w' share an XCD when w = w' (mod 8) under round-robin dispatch
+        pairs = [(0, 8), (3, 11), (5, 13), (0, 1), (0, 4), (2, 7), (1, 6)]
+        res = []
+        for a, b in pairs:
+            r = da.detattn_xcd_handoff(a, b, 8192)
+            r.update(wg_a=a, wg_b=b, same_xcd=r["xcd_a"] == r["xcd_b"])
+            res.append(r)
+            log(f"[bench] hand-off wg {a} (XCD {r['xcd_a']}) <-> wg {b} (XCD {r['xcd_b']}): {r['ns']:.0f} ns, "
+                f"{r['cycles']:.0f} cycles per round trip")
+        same = [r["ns"] for r in res if r["same_xcd"] and not r["timed_out"]]
+        cross = [r["ns"] for r in res if not r["same_xcd"] and not r["timed_out"]]
+        print(json.dumps({"xcd_handoff": res, "round_trip_ns_same_xcd": sum(same) / len(same) if same else None,
+                          "round_trip_ns_cross_xcd": sum(cross) / len(cross) if cross else None}), flush=True)
+        return
 
     if args.shape:
         f = args.shape.split(",")

@@ -75,6 +75,8 @@ def lib():
         L.attn_bwd_deterministic_ex.restype = ctypes.c_int
         L.attn_bwd_deterministic_noalloc.argtypes = [vp] * 9 + [Shape, ctypes.c_int, ctypes.c_int, vp]
         L.attn_bwd_deterministic_noalloc.restype = ctypes.c_int
+        L.detattn_xcd_handoff.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp]
+        L.detattn_xcd_handoff.restype = ctypes.c_int
         L.detattn_bwd_plan.argtypes = [Shape, ctypes.c_int, ctypes.c_int, ctypes.POINTER(BwdOptions),
                                        ctypes.POINTER(Plan)]
         L.detattn_bwd_plan.restype = ctypes.c_int
@@ -250,3 +252,18 @@ def detattn_schedule_item(schedule, causal, n_q, n_kv, item, ring=0):
 
 def detattn_schedule_items_per_head(schedule, causal, n_q, n_kv):
     return int(lib().detattn_schedule_items_per_head(SCHEDULES[schedule], 1 if causal else 0, n_q, n_kv))
+
+
+def detattn_xcd_handoff(wg_a, wg_b, round_trips=4096, device="cuda"):
+    """Round-trip latency of a device-scope flag passed between workgroups wg_a
+    and wg_b (the ordered dQ hand-off's mechanism): {"ns", "cycles" per round
+    trip, "xcd_a", "xcd_b", "timed_out"}. Synchronises the current stream."""
+    scratch = torch.empty(256, dtype=torch.uint8, device=device)
+    out = torch.zeros(5, dtype=torch.int64, device=device)
+    st = lib().detattn_xcd_handoff(int(wg_a), int(wg_b), int(round_trips), _ptr(scratch), _ptr(out), _stream(None))
+    if st != 0:
+        raise DetAttnError(st, "detattn_xcd_handoff")
+    torch.cuda.synchronize()
+    r = out.cpu().tolist()
+    n = round_trips - 1
+    return {"ns": r[0] * 10.0 / n, "cycles": r[1] / n, "xcd_a": r[2], "xcd_b": r[3], "timed_out": bool(r[4])}

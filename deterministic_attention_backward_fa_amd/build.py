@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libdetattn.so")
 ARCH = "gfx950"
 
 MAIN_SOURCES = ["bwd_d64.hip", "bwd_d128.hip", "bwd_d64_trace.hip", "bwd_d128_trace.hip"]
-SOURCES = ["capi.cpp", "kernels_misc.hip", "noalloc.hip"] + MAIN_SOURCES
+SOURCES = ["capi.cpp", "kernels_misc.hip", "noalloc.hip", "xcd_probe.hip"] + MAIN_SOURCES
 # The main backward kernel keeps MFMA results the VALU reads in VGPRs (its
 # AGPR-resident accumulations are written as explicit AGPR-form MFMAs).
 PER_SOURCE = {src: ["-mllvm", "-amdgpu-mfma-vgpr-form"] for src in MAIN_SOURCES}

@@ -238,6 +238,23 @@ int attn_bwd_deterministic_noalloc(const void* q, const void* k, const void* v, 
                                    const float* lse, void* dq, void* dk, void* dv, detattn_shape_t shape,
                                    detattn_mask_t mask, detattn_schedule_t schedule, void* stream);
 
+/*
+ * Measurement aid for the XCD placement study (not part of the backward): the
+ * round-trip latency of a flag passed between workgroups wg_a and wg_b of a
+ * small cooperative grid through device-scope atomics, the mechanism of the
+ * ordered dQ hand-off (the pages' inter-SM hand-off: nachedeu.com news piece;
+ * zskr.cn explainer section 4.2). With round-robin dispatch, workgroups whose
+ * indices agree modulo 8 share an XCD.
+ *  scratch : device, 256 bytes, 256-byte aligned (overwritten)
+ *  result  : device, 5 uint64 (asynchronous; read after synchronising `stream`):
+ *            [0] s_memrealtime ticks (100 MHz) and [1] shader cycles over
+ *            round_trips - 1 round trips, [2] XCD of wg_a, [3] XCD of wg_b,
+ *            [4] 1 if a wait gave up (after 1 s; the kernel always ends)
+ *  wg_a, wg_b < 64 and distinct; 2 <= round_trips <= 65536 (all within the 1 s bound).
+ * Returns DETATTN_ERR_INVALID_ARG or DETATTN_ERR_HIP before launching on errors.
+ */
+int detattn_xcd_handoff(int wg_a, int wg_b, int round_trips, void* scratch, uint64_t* result, void* stream);
+
 /* Resolve tiles, grid and rings for a call without launching anything.
  * Needs a HIP device for the compute-unit count unless options->grid > 0. */
 int detattn_bwd_plan(detattn_shape_t shape, detattn_mask_t mask, detattn_schedule_t schedule,

@@ -182,3 +182,40 @@ def closed_form(schedule: str, mask: str, n: int, m: int, c, r):
     if schedule in ("serial_ascending", "descending_q") and mask == "full":
         return m * n * (c + r) + (n - 1) * r
     raise ValueError((schedule, mask))
+
+
+def timeline(schedule: str, mask: str, n: int, m: int, c, r, n_sm: Optional[int] = None):
+    """Per-SM schedule of the model: {sm: [(start, compute_end, reduce_start, end, head, i, j), ...]}
+    in start order, from the event depths (earliest times). A gap between
+    compute_end and reduce_start is the tile's wait for its turn in the dQ order."""
+    g, assignment = build(schedule, mask, n, m, c, r, n_sm)
+    d = g.depths()
+    its = S.items(schedule, mask, n, n)
+    per: Dict[int, list] = defaultdict(list)
+    for (h, it_idx), sm in assignment.items():
+        for (i, j) in its[it_idx]:
+            per[sm].append((d[("Cs", h, i, j)], d[("Ce", h, i, j)], d[("Rs", h, i, j)], d[("Re", h, i, j)], h, i, j))
+    for sm in per:
+        per[sm].sort()
+    return dict(per)
+
+
+def render(per, unit=1) -> str:
+    """Text figure of a timeline: one row per SM, one character per `unit` of
+    time; a computing tile shows its Q tile index (base 36), its reduce 'r', a
+    wait for the dQ turn '.', an idle SM ' '."""
+    end = max(t[3] for tl in per.values() for t in tl)
+    width = int(-(-end // unit))
+    rows = []
+    digits = "0123456789abcdefghijklmnopqrstuvwxyz"
+    for sm in sorted(per):
+        row = [" "] * width
+        for (s, ce, rs, e, h, i, j) in per[sm]:
+            for x in range(int(s // unit), int(-(-ce // unit))):
+                row[x] = digits[i % 36]
+            for x in range(int(ce // unit), int(-(-rs // unit))):
+                row[x] = "."
+            for x in range(int(rs // unit), int(-(-e // unit))):
+                row[x] = "r"
+        rows.append(f"SM{sm:<3d}|" + "".join(row) + "|")
+    return "\n".join(rows)

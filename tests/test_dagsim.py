@@ -77,3 +77,27 @@ def test_lemma1_zero_weight_edge():
                 assert unchanged == (base[u] <= base[v])
                 checked[unchanged] += 1
     assert checked[True] > 100 and checked[False] > 100
+
+
+def test_four_sm_timelines_reconstruct_the_shift_figures():
+    """The pages illustrate the shift schedule on 4 SMs with a figure that the
+    text lost (zskr.cn explainer 3.2; the symmetric form, 3.3). The model's
+    timelines at n = 4, m = 2, c = 3, r = 1: under shift SM j computes Q tiles
+    j, j+1, ... (mod 4) of its KV tile, head after head, with no wait; under
+    symmetric shift two heads run side by side, each SM holding one pair item of
+    n + 1 = 5 tiles back to back (the derived fold: pair p = KV tiles p, 3 - p)."""
+    c, r = 3, 1
+    per = G.timeline("shift", "full", 4, 2, c, r)
+    assert sorted(per) == [0, 1, 2, 3]
+    for sm, tl in per.items():
+        assert [(h, i, j) for (_, _, _, _, h, i, j) in tl] == [(h, (sm + t) % 4, sm) for h in range(2) for t in range(4)]
+        for k, (s, ce, rs, e, *_rest) in enumerate(tl):
+            assert (s, ce, rs, e) == (k * (c + r), k * (c + r) + c, k * (c + r) + c, (k + 1) * (c + r))
+    fig = G.render(per)
+    assert fig.splitlines()[1] == "SM1  |111r222r333r000r111r222r333r000r|"
+    per = G.timeline("symmetric_shift", "causal", 4, 2, c, r)
+    golden = {0: [(2, 0), (3, 0), (0, 0), (1, 0), (3, 3)], 1: [(3, 1), (2, 1), (1, 1), (3, 2), (2, 2)]}
+    for sm, tl in per.items():
+        assert [(i, j) for (*_x, h, i, j) in tl] == golden[sm % 2]
+        assert all(h == sm // 2 for (*_x, h, i, j) in tl)
+        assert [t[0] for t in tl] == [k * (c + r) for k in range(5)]   # no waits, no idle time
