@@ -6,11 +6,11 @@
 namespace detattn {
 namespace {
 
-template <int D, int BQ, int BKV, bool CAUSAL, int DQM, bool TRACE>
+template <int D, int BQ, int BKV, bool CAUSAL, int DQM, bool TRACE, bool PAIR = false>
 MainInfo info_of() {
   static const MainInfo cached = [] {
     MainInfo m;
-    auto fn = &bwd_main_kernel<D, BQ, BKV, CAUSAL, DQM, TRACE>;
+    auto fn = &bwd_main_kernel<D, BQ, BKV, CAUSAL, DQM, TRACE, PAIR>;
     m.func = reinterpret_cast<const void*>(fn);
     m.lds_bytes = MainCfg<D, BQ, BKV>::LDS_BYTES;
     int occ = 0;
@@ -39,6 +39,17 @@ MainInfo pick_mode(int dqm) {
 template <int D, bool TRACE, int BQ, int BKV>
 MainInfo pick(int causal, int dqm) {
   return causal ? pick_mode<D, TRACE, BQ, BKV, true>(dqm) : pick_mode<D, TRACE, BQ, BKV, false>(dqm);
+}
+
+// The resident-pair instances (symmetric shift, causal; ordered dQ modes only).
+template <int D, int BQ, int BKV>
+MainInfo pick_pair(int dqm) {
+  switch (dqm) {
+    case kDqOrderedRmw: return info_of<D, BQ, BKV, true, kDqOrderedRmw, false, true>();
+    case kDqOrderedAtomic: return info_of<D, BQ, BKV, true, kDqOrderedAtomic, false, true>();
+    case kDqLocalRmw: return info_of<D, BQ, BKV, true, kDqLocalRmw, false, true>();
+    default: return MainInfo{nullptr, 0, 0};
+  }
 }
 
 }  // namespace

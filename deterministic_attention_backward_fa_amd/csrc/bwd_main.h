@@ -146,6 +146,11 @@ struct MainCfg {
   static constexpr int OFF_K = OFF_B0 + BUF;
   static constexpr int OFF_V = OFF_K + KB;
   static constexpr int TILE_END = OFF_B0 + NBUF * BUF;
+  // Resident-pair variant of symmetric shift: the pair's second column K, V
+  // are staged next to the first (both within the tile buffers)
+  static constexpr int OFF_K2 = OFF_V + KB;
+  static constexpr int OFF_V2 = OFF_K2 + KB;
+  static constexpr bool PAIR_FITS = OFF_V2 + KB <= TILE_END;
   static constexpr int DMA_Q = BQ * (NCH + 1) / 64;  // 1 KB DMA instructions per padded Q/dO tile
   static constexpr int DMA_K = BKV * (NCH + 1) / 64;
   static constexpr int DMA_QW = (DMA_Q + 3) / 4;     // per wave, at most
@@ -489,9 +494,15 @@ __device__ __forceinline__ void dma16(const void* gsrc, void* lds) {
   __builtin_amdgcn_global_load_lds((gbl_void*)gsrc, (lds_void*)lds, 16, 0, 0);
 }
 
-template <int D, int BQ, int BKV, bool CAUSAL, int DQM, bool TRACE>
+// PAIR (symmetric shift only): both columns of a pair item keep their K, V
+// and dK, dV in registers for the whole item (the pages' alternative to
+// holding one column at a time), so the item has no column switch: the visits,
+// the ranks and every result bit are those of the sequential form.
+template <int D, int BQ, int BKV, bool CAUSAL, int DQM, bool TRACE, bool PAIR>
 __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   using C = MainCfg<D, BQ, BKV>;
+  static_assert(!PAIR || C::PAIR_FITS, "pair K/V staging");
+  constexpr int NSET = PAIR ? 2 : 1;  // register sets of K, V, K^T, dK, dV
   using SA = StreamA<C>;
   constexpr int PF = DETATTN_PF;  // LDS operand loads run this many MFMAs ahead
   constexpr int RING = PF + 2;  // operand registers; a slot is reloaded two MFMAs after its last reader
@@ -740,13 +751,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
 
 
     // K_j, V_j into their LDS tiles (asynchronous)
-    auto dma_kv = [&](long long kv_head, int kv_j) {
+    auto dma_kv = [&](long long kv_head, int kv_j, int off_k = C::OFF_K) {
       const unsigned char* gk = reinterpret_cast<const unsigned char*>(a.k + kv_head + (long long)kv_j * BKV * D);
       const unsigned char* gv = reinterpret_cast<const unsigned char*>(a.v + kv_head + (long long)kv_j * BKV * D);
       for (int ins = w; ins < C::DMA_K; ins += 4) {
         const int go = dma_goff<C::NCH>(ins, lane);
-        dma16(gk + go, smem + C::OFF_K + ins * 1024);
-        dma16(gv + go, smem + C::OFF_V + ins * 1024);
+        dma16(gk + go, smem + off_k + ins * 1024);
+        dma16(gv + go, smem + off_k + (C::OFF_V - C::OFF_K) + ins * 1024);
       }
     };
     // The second column's K, V load while the first column's dK, dV go out
@@ -762,6 +773,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
         int j0;
         const SegWalk w0 = sc.walk(it, 0, j0);
         dma_kv(head_off, j0);
+        if constexpr (PAIR) dma_kv(head_off, sc.seg_kv(it, 1), C::OFF_K2);
         dma_q(0, head_off, bhS, w0.i);
       }
       if (!registered_ring()) {
@@ -779,28 +791,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     }
     if (gidx < 0) return;
 
-    for (int seg = 0; seg < sc.segments(); ++seg) {
-    const int t_begin = sc.seg_begin(it, seg), t_end = sc.seg_end(it, seg);
-    int j;
-    SegWalk cur = sc.walk(it, seg, j);  // at step t_begin
-    const int i0 = cur.i;
-    // ---- segment prologue: K_j, V_j (the second column of a symmetric pair has
-    // them on their way already) and the first Q tile ----
-    if (!first_loaded) {
-      if (seg == 0) dma_kv(head_off, j);
-      dma_q(0, head_off, bhS, i0);
-    }
-    first_loaded = false;
-    wait_vm_all();
-    __syncthreads();
+    // the resident pair's two register sets (the one-column form declares its
+    // set inside the segment body, live for that column only)
+    bf16x8 kB_[NSET][C::KD], vB_[NSET][C::KD], kTB_[NSET][C::KKV * C::DW];
+    f32x16 dKacc_[NSET][C::ND], dVacc_[NSET][C::ND];
     // K_j, V_j (MFMA B operands of S, dP) and K_j transposed (B operand of the
-    // dQ partial) go straight into AGPRs
-    bf16x8 kB[C::KD], vB[C::KD], kTB[C::KKV * C::DW];
-    {
-      const uint32_t ak = lbase + C::OFF_K + rperm(32 * wk + c32) * C::PD + g * 16;
+    // dQ partial) from their LDS staging (at off_k) straight into AGPRs
+    auto load_kv_regs = [&](bf16x8(&kB)[C::KD], bf16x8(&vB)[C::KD], bf16x8(&kTB)[C::KKV * C::DW], int off_k) {
+      const uint32_t ak = lbase + off_k + rperm(32 * wk + c32) * C::PD + g * 16;
       const uint32_t av = ak + (C::OFF_V - C::OFF_K);
       // K transposed (non-permuted K order): logical rows 8g + j at physical 4j + 2g, rows + 4 at + 1
-      const uint32_t akt = lbase + C::OFF_K + (4 * (s16 >> 2) + 2 * g) * C::PD + trcol + 64 * nbq;
+      const uint32_t akt = lbase + off_k + (4 * (s16 >> 2) + 2 * g) * C::PD + trcol + 64 * nbq;
       constexpr int NT = C::KKV * C::DW;  // K^T fragments: K step s, column block n at s * DW + n
       u32x4 kq[C::KD], vq[C::KD];
       u32x2 tlo[NT], thi[NT];
@@ -847,17 +848,56 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
         kTB[x] = as_bf16x8(cat2(tlo[x], thi[x]));
         pin_agpr(kTB[x]);
       }
+    };
+    auto zero_acc = [&](f32x16(&dK)[C::ND], f32x16(&dV)[C::ND]) {
+#pragma unroll
+      for (int n = 0; n < C::ND; ++n) {
+        dK[n] = f32x16{};
+        dV[n] = f32x16{};
+        pin_agpr(dK[n]);
+        pin_agpr(dV[n]);
+      }
+    };
+
+    auto seg_body = [&](auto setc, int seg) {
+    constexpr int SET = decltype(setc)::value;
+    bf16x8 kB_col[C::KD], vB_col[C::KD], kTB_col[C::KKV * C::DW];
+    f32x16 dK_col[C::ND], dV_col[C::ND];
+    bf16x8(&kB)[C::KD] = PAIR ? kB_[SET] : kB_col;
+    bf16x8(&vB)[C::KD] = PAIR ? vB_[SET] : vB_col;
+    bf16x8(&kTB)[C::KKV * C::DW] = PAIR ? kTB_[SET] : kTB_col;
+    f32x16(&dKacc)[C::ND] = PAIR ? dKacc_[SET] : dK_col;
+    f32x16(&dVacc)[C::ND] = PAIR ? dVacc_[SET] : dV_col;
+    const int t_begin = sc.seg_begin(it, seg), t_end = sc.seg_end(it, seg);
+    int j;
+    SegWalk cur = sc.walk(it, seg, j);  // at step t_begin
+    const int i0 = cur.i;
+    // ---- segment prologue: K_j, V_j (the second column of a symmetric pair has
+    // them on their way already) and the first Q tile ----
+    if (!first_loaded) {
+      if (seg == 0) {
+        dma_kv(head_off, j);
+        if constexpr (PAIR) dma_kv(head_off, sc.seg_kv(it, 1), C::OFF_K2);
+      }
+      dma_q(0, head_off, bhS, i0);
+    }
+    first_loaded = false;
+    wait_vm_all();
+    __syncthreads();
+    if constexpr (PAIR) {
+      // the pair's two columns enter registers at the item's start
+      if constexpr (SET == 0) {
+        load_kv_regs(kB_[0], vB_[0], kTB_[0], C::OFF_K);
+        load_kv_regs(kB_[1], vB_[1], kTB_[1], C::OFF_K2);
+        zero_acc(dKacc_[0], dVacc_[0]);
+        zero_acc(dKacc_[1], dVacc_[1]);
+      }
+    } else {
+      load_kv_regs(kB, vB, kTB, C::OFF_K);
+      zero_acc(dKacc, dVacc);
     }
     // K, V are in registers: buffer 1 is free for the next Q tile
     lds_barrier();
-    f32x16 dKacc[C::ND], dVacc[C::ND];
-#pragma unroll
-    for (int n = 0; n < C::ND; ++n) {
-      dKacc[n] = f32x16{};
-      dVacc[n] = f32x16{};
-      pin_agpr(dKacc[n]);
-      pin_agpr(dVacc[n]);
-    }
     trace_rec(6, t_begin, gidx);
 
     int t = t_begin;
@@ -1317,17 +1357,34 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       pend = nullptr;
     }
     __syncthreads();
+    if constexpr (PAIR && SET == 0) {
+      // resident pair: the first column's dK, dV stay in registers until the item ends
+      trace_rec(7, t_end, gidx);
+      return;
+    }
     // every wave's LDS reads and DMA of this column are done: the item's next
     // column's K, V go out now, under the stores below
-    if (seg + 1 < sc.segments()) dma_kv(head_off, sc.seg_kv(it, seg + 1));
+    if (!PAIR && seg + 1 < sc.segments()) dma_kv(head_off, sc.seg_kv(it, seg + 1));
     {
       float* red = reinterpret_cast<float*>(smem);
       __bf16* sOut = reinterpret_cast<__bf16*>(smem + C::RED_BYTES);
+      if constexpr (PAIR) {
+        const int j0 = sc.seg_kv(it, 0);
+        store_column<C>(dKacc_[0], a.scale, a.dk + head_off + (long long)j0 * BKV * D, red, sOut, wk, wq, lane);
+        store_column<C>(dVacc_[0], 1.f, a.dv + head_off + (long long)j0 * BKV * D, red, sOut, wk, wq, lane);
+      }
       store_column<C>(dKacc, a.scale, a.dk + head_off + (long long)j * BKV * D, red, sOut, wk, wq, lane);
       store_column<C>(dVacc, 1.f, a.dv + head_off + (long long)j * BKV * D, red, sOut, wk, wq, lane);
     }
     trace_rec(7, t_end, gidx);
-    }  // segments
+    };  // segment body
+
+    if constexpr (PAIR) {
+      seg_body(std::integral_constant<int, 0>{}, 0);
+      seg_body(std::integral_constant<int, 1>{}, 1);
+    } else {
+      for (int seg = 0; seg < sc.segments(); ++seg) seg_body(std::integral_constant<int, 0>{}, seg);
+    }
   }  // items
 }
 

@@ -132,7 +132,8 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
   std::memset(&o, 0, sizeof(o));
   if (opt) o = *opt;
   if (o.block_q < 0 || o.block_kv < 0 || o.grid < 0 || o.xcd_remap < 0 || o.xcd_remap > 2 || o.dq_mode < 0 ||
-      o.dq_mode > 3 || o.ring_size < 0 || o.dispatch < 0 || o.dispatch > 2)
+      o.dq_mode > 3 || o.ring_size < 0 || o.dispatch < 0 || o.dispatch > 2 || o.pair_columns < 0 ||
+      o.pair_columns > 1)
     return DETATTN_ERR_INVALID_ARG;
   int bq, bkv;
   default_tiles(s.D, s.S, bq, bkv);
@@ -245,7 +246,9 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
           : pub_dqm == DETATTN_DQ_XCD_LOCAL_RMW ? kDqLocalRmw
                                                  : kDqOrderedRmw;
   }
-  const MainInfo info = main_info(s.D, bq, bkv, causal, dqm, false);
+  // the resident pair is symmetric shift's; it has no traced instance
+  if (o.pair_columns && (sch != DETATTN_SYMMETRIC_SHIFT || o.trace)) return DETATTN_ERR_UNSUPPORTED;
+  const MainInfo info = main_info(s.D, bq, bkv, causal, dqm, false, o.pair_columns != 0);
   if (!info.func) return DETATTN_ERR_UNSUPPORTED;
   P.pub.block_q = bq;
   P.pub.block_kv = bkv;
@@ -258,6 +261,7 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
   P.pub.dq_mode = pub_dqm;
   P.pub.cooperative = ring_sched ? 1 : 0;
   P.pub.schedule = (int32_t)sch;
+  P.pub.pair_columns = o.pair_columns;
   P.causal = causal;
   P.sch = (int)sch;
   P.sc = sc;
@@ -384,6 +388,7 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
   M.dq_mode = P.dqm_internal;
   M.grid = P.pub.grid;
   M.cooperative = P.pub.cooperative;
+  M.pair = P.pub.pair_columns;
   if (options && options->main_begin_event &&
       hipEventRecord(static_cast<hipEvent_t>(options->main_begin_event), st_) != hipSuccess)
     return DETATTN_ERR_HIP;

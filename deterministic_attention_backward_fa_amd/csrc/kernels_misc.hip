@@ -92,7 +92,7 @@ hipError_t launch_convert(int D, const float* acc, __bf16* dq, long long rows, f
 }
 
 hipError_t launch_main(const MainLaunch& L, hipStream_t st) {
-  MainInfo info = main_info(L.D, L.BQ, L.BKV, L.causal, L.dq_mode, L.args.trace != nullptr);
+  MainInfo info = main_info(L.D, L.BQ, L.BKV, L.causal, L.dq_mode, L.args.trace != nullptr, L.pair != 0);
   if (!info.func) return hipErrorInvalidDeviceFunction;
   BwdArgs args = L.args;
   void* kargs[] = {(void*)&args};

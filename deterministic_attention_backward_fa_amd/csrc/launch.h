@@ -12,6 +12,7 @@ namespace detattn {
 struct MainLaunch {
   BwdArgs args;
   int D, BQ, BKV, causal, dq_mode;  // dq_mode: DqMode
+  int pair;                          // resident-pair symmetric shift instance
   int grid;
   int cooperative;
 };
@@ -24,13 +25,16 @@ struct MainInfo {
 };
 
 MainInfo main_info_d64(int BQ, int BKV, int causal, int dq_mode);
+MainInfo main_info_d64_pair(int BQ, int BKV, int dq_mode);
 MainInfo main_info_d128(int BQ, int BKV, int causal, int dq_mode);
 MainInfo main_info_d64_trace(int BQ, int BKV, int causal, int dq_mode);
 MainInfo main_info_d128_trace(int BQ, int BKV, int causal, int dq_mode);
 
 // The instance for head dimension D (64 or 128); `trace` selects the variant
-// that writes the per-tile phase trace.
-inline MainInfo main_info(int D, int BQ, int BKV, int causal, int dq_mode, bool trace) {
+// that writes the per-tile phase trace, `pair` the resident-pair symmetric
+// shift (built at D = 64 with 64 x 64 tiles, causal, untraced).
+inline MainInfo main_info(int D, int BQ, int BKV, int causal, int dq_mode, bool trace, bool pair = false) {
+  if (pair) return (D == 64 && causal && !trace) ? main_info_d64_pair(BQ, BKV, dq_mode) : MainInfo{nullptr, 0, 0};
   if (D == 64) return trace ? main_info_d64_trace(BQ, BKV, causal, dq_mode) : main_info_d64(BQ, BKV, causal, dq_mode);
   if (D == 128) return trace ? main_info_d128_trace(BQ, BKV, causal, dq_mode) : main_info_d128(BQ, BKV, causal, dq_mode);
   return MainInfo{nullptr, 0, 0};

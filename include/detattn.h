@@ -150,6 +150,11 @@ typedef struct {
                                 device-scope adds (measured faster than adds kept in one XCD's L2). The
                                 accumulation order of the ordered schedules, rank = KV tile, is the same
                                 in both. Ignored by SHIFT / SYMMETRIC_SHIFT (always rings). */
+  int32_t pair_columns;      /* SYMMETRIC_SHIFT: 1 = both columns of a pair item keep their K, V and dK, dV
+                                accumulators in registers for the whole item (the pages' alternative to one
+                                column at a time; no column switch inside an item, same visits, order and
+                                bits); built for D = 64 with 64 x 64 tiles, else UNSUPPORTED. 0 = one
+                                column's set at a time (default). */
 } detattn_bwd_options_t;
 
 /* Phase ids written into the optional trace (low 8 bits of the second word). */
@@ -177,6 +182,7 @@ typedef struct {
                           DETATTN_DQ_XCD_LOCAL_RMW = atomic adds in one XCD's L2 (rings of one XCD) */
   int32_t cooperative; /* 1 if launched as a cooperative (co-resident) grid */
   int32_t schedule;    /* the schedule that runs (AUTO resolved) */
+  int32_t pair_columns; /* 1 if the resident-pair form of symmetric shift runs */
 } detattn_plan_t;
 
 /*

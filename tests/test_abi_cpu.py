@@ -301,3 +301,18 @@ def test_noalloc_entry_refuses_before_any_hip_call():
     # the largest workload shapes here fit: B*H*S*D = 2^25
     assert da.detattn_bwd_workspace_bytes(1, 32, 8192, 128) <= da.NOALLOC_SCRATCH_BYTES
     assert da.detattn_bwd_workspace_bytes(4, 16, 8192, 64) <= da.NOALLOC_SCRATCH_BYTES
+
+
+def test_resident_pair_option():
+    """pair_columns selects the resident-pair form of symmetric shift, built at
+    D = 64 with 64 x 64 tiles; other schedules, tiles or head dimensions are
+    UNSUPPORTED."""
+    kv64 = dict(block_q=64, block_kv=64, grid=256)
+    p = da.detattn_bwd_plan(1, 2, 1024, 64, True, "symmetric_shift", pair_columns=True, **kv64)
+    assert p["pair_columns"] == 1 and p["schedule"] == da.SCHEDULES["symmetric_shift"]
+    assert da.detattn_bwd_plan(1, 2, 1024, 64, True, "symmetric_shift", **kv64)["pair_columns"] == 0
+    for args, kw in [((1, 2, 1024, 64, True, "descending_q"), kv64),
+                     ((1, 2, 1024, 64, True, "symmetric_shift"), dict(grid=256)),     # 128 x 128 tiles
+                     ((1, 2, 1024, 128, True, "symmetric_shift"), kv64)]:            # D = 128: does not fit
+        with pytest.raises(da.DetAttnError):
+            da.detattn_bwd_plan(*args, pair_columns=True, **kw)

@@ -299,3 +299,45 @@ def test_traced_instances_match_oracle_and_untraced_bits(case):
         for w in range(plan["grid"]):
             ts = t[w, :, 0][used[w]]
             assert torch.all(ts[1:] >= ts[:-1]), (sched, w)
+
+
+PAIR_CASES = [
+    # (B, H, S, D, seed, ring sizes): causal, 64 x 64 tiles, D = 64
+    (1, 2, 512, 64, 61, (0, 2)),
+    (2, 3, 1024, 64, 62, (0, 4)),
+    (1, 1, 2048, 64, 63, (0,)),
+]
+
+
+@pytest.mark.parametrize("case", PAIR_CASES, ids=lambda c: f"B{c[0]}H{c[1]}S{c[2]}D{c[3]}")
+def test_resident_pair_symmetric_shift_equals_sequential(case):
+    """Symmetric shift with both columns of a pair item resident in registers
+    (the register-pressure alternative the pages discuss) visits the same tiles
+    in the same order as the one-column-at-a-time form: every output bit is the
+    same, it meets the oracle, and it repeats bit for bit."""
+    B, H, S, D, seed, rings = case
+    opts = dict(block_q=64, block_kv=64)
+    scale = 1.0 / math.sqrt(D)
+    cpu, (q, k, v, do, o, lse) = inputs(B, H, S, D, seed, True)
+    dq_r, dk_r, dv_r, _, _ = _oracle(cpu, True, scale)
+    ws = da.alloc_workspace(B, H, S, D)
+    for G in rings:
+        ring = dict(ring_size=G) if G else {}
+        plan = da.detattn_bwd_plan(B, H, S, D, True, "symmetric_shift", pair_columns=True, **opts, **ring)
+        assert plan["pair_columns"] == 1
+        say(f"[resident pair] {case[:4]} ring {G or 'default'} plan {plan}")
+        seq = [t.clone() for t in da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=True, schedule="symmetric_shift",
+                                                            workspace=ws, **opts, **ring)]
+        pair = [t.clone() for t in da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=True,
+                                                             schedule="symmetric_shift", workspace=ws,
+                                                             pair_columns=True, **opts, **ring)]
+        assert da.detattn_device_status(ws) == 0
+        assert all(same_bits(a_, b_) for a_, b_ in zip(seq, pair))
+        for name, got, want in (("dq", pair[0], dq_r), ("dk", pair[1], dk_r), ("dv", pair[2], dv_r)):
+            e = rel_err(got.float().cpu().numpy(), want)
+            assert e <= TOL, f"resident pair {name} rel err {e:.3e}"
+        for _ in range(9):
+            again = da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=True, schedule="symmetric_shift", workspace=ws,
+                                              pair_columns=True, **opts, **ring)
+            assert all(same_bits(a_, b_) for a_, b_ in zip(pair, again))
+        assert da.detattn_device_status(ws) == 0
