@@ -205,6 +205,8 @@ def main():
                     help="workgroups per ring of the shift schedules (0 = library default)")
     ap.add_argument("--pair-columns", action="store_true",
                     help="symmetric shift with both columns of a pair item resident in registers (D = 64, 64x64 tiles)")
+    ap.add_argument("--cooperative-launch", action="store_true",
+                    help="ring dispatch through HIP's cooperative launch instead of a plain launch")
     ap.add_argument("--trace", action="store_true", help="log the headline schedule's per-tile phase breakdown")
     ap.add_argument("--trace-gantt", action="store_true",
                     help="with --trace: also print a text timeline of the traced workgroups")
@@ -281,6 +283,8 @@ def main():
             opts["dispatch"] = args.dispatch
         if args.pair_columns and sched == "symmetric_shift":
             opts["pair_columns"] = True
+        if args.cooperative_launch:
+            opts["cooperative_launch"] = True
         return opts
 
     for sched in scheds:
@@ -352,7 +356,8 @@ def main():
     # workload (every schedule) and reports it beside the causal headline.
     default_run = (not args.shape and args.config == "causal_b1_h32_s8192_d128" and not args.only_headline
                    and not tile_opts and not args.ring_size and args.dispatch == "default"
-                   and args.dq_mode == "default" and not args.schedule and not args.pair_columns)
+                   and args.dq_mode == "default" and not args.schedule and not args.pair_columns
+                   and not args.cooperative_launch)
     if default_run and not args.no_companion:
         cB, cH, cS, cD, ccausal, cseed = CONFIGS["full_b2_h32_s4096_d128"]
         log(f"[bench] companion full_b2_h32_s4096_d128: generating inputs (seed {cseed})")

@@ -133,7 +133,7 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
   if (opt) o = *opt;
   if (o.block_q < 0 || o.block_kv < 0 || o.grid < 0 || o.xcd_remap < 0 || o.xcd_remap > 2 || o.dq_mode < 0 ||
       o.dq_mode > 3 || o.ring_size < 0 || o.dispatch < 0 || o.dispatch > 2 || o.pair_columns < 0 ||
-      o.pair_columns > 1)
+      o.pair_columns > 1 || o.cooperative_launch < 0 || o.cooperative_launch > 1)
     return DETATTN_ERR_INVALID_ARG;
   int bq, bkv;
   default_tiles(s.D, s.S, bq, bkv);
@@ -259,7 +259,7 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
   P.pub.ring = ring;
   P.pub.rings = rings;
   P.pub.dq_mode = pub_dqm;
-  P.pub.cooperative = ring_sched ? 1 : 0;
+  P.pub.cooperative = ring_sched && o.cooperative_launch == 1 ? 1 : 0;
   P.pub.schedule = (int32_t)sch;
   P.pub.pair_columns = o.pair_columns;
   P.causal = causal;
@@ -324,6 +324,14 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
   Plan P;
   const int st = make_plan(s, mask, schedule, options, P);
   if (st != DETATTN_OK) return st;
+  if (P.pub.ring > 0 && !P.pub.cooperative) {
+    // a plain launch of ring dispatch: the whole grid must fit the device at once
+    const MainInfo mi = main_info(s.D, P.pub.block_q, P.pub.block_kv, P.causal, P.dqm_internal,
+                                  options && options->trace, P.pub.pair_columns != 0);
+    const int cus = device_cus();
+    if (cus <= 0 || mi.occupancy <= 0) return DETATTN_ERR_HIP;
+    if (P.pub.grid > cus * mi.occupancy) return DETATTN_ERR_UNSUPPORTED;
+  }
   const long long BH = (long long)s.B * s.H;
   WsLayout L(BH, s.S, s.D);
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < L.total)

@@ -155,6 +155,17 @@ typedef struct {
                                 column at a time; no column switch inside an item, same visits, order and
                                 bits); built for D = 64 with 64 x 64 tiles, else UNSUPPORTED. 0 = one
                                 column's set at a time (default). */
+  int32_t cooperative_launch; /* ring dispatch needs every workgroup of the grid resident at once (a ring's
+                                workgroups wait on each other's dQ flags). 0 = default: a plain launch of a
+                                grid no larger than the device's resident capacity (compute units x
+                                occupancy; a larger explicit `grid` is UNSUPPORTED), which an otherwise idle
+                                device runs co-resident; ring calls running at once on other streams of the
+                                same device can then hold each other's workgroups back until a bounded wait
+                                times out (DETATTN_DEVICE_TIMEOUT, results not deterministic). 1 = HIP's
+                                cooperative launch, which guarantees co-residency whatever else runs on the
+                                device, at about 15 us of added launch latency per call. Ticket dispatch
+                                needs neither (a ticket is only taken by a running workgroup) and always
+                                launches plainly. */
 } detattn_bwd_options_t;
 
 /* Phase ids written into the optional trace (low 8 bits of the second word). */
@@ -180,7 +191,7 @@ typedef struct {
   int32_t rings;       /* rings running at once, else 0 */
   int32_t dq_mode;     /* resolved detattn_dq_mode_t; ATOMIC_NONDET: 0 = device-scope atomic adds,
                           DETATTN_DQ_XCD_LOCAL_RMW = atomic adds in one XCD's L2 (rings of one XCD) */
-  int32_t cooperative; /* 1 if launched as a cooperative (co-resident) grid */
+  int32_t cooperative; /* 1 if launched with HIP's cooperative launch (ring dispatch with cooperative_launch = 1) */
   int32_t schedule;    /* the schedule that runs (AUTO resolved) */
   int32_t pair_columns; /* 1 if the resident-pair form of symmetric shift runs */
 } detattn_plan_t;

@@ -122,9 +122,12 @@ def test_default_tiles_and_rings(cfg):
     n_kv = S // bkv
     items = n_kv if sched == "shift" else n_kv // 2
     ring = min(items, 32)  # one XCD's workgroups; larger heads take their items in rounds
-    assert p["ring"] == ring and p["cooperative"] == 1
+    assert p["ring"] == ring and p["cooperative"] == 0  # plain launch unless asked
     assert p["grid"] == p["rings"] * ring <= 256
     assert p["rings"] >= 1
+    c = da.detattn_bwd_plan(B, H, S, D, causal, sched, grid=256, cooperative_launch=True)
+    assert c["cooperative"] == 1 and {k: c[k] for k in c if k != "cooperative"} == \
+        {k: p[k] for k in p if k != "cooperative"}
 
 
 def test_ticket_plan_caps_grid_at_items():
@@ -141,17 +144,17 @@ def test_serial_descending_atomic_rings(sched):
     atomic reference takes rings (adds in one XCD's L2) only when asked."""
     ask = {"dispatch": "ring"} if sched == "atomic_nondet" else {}
     p = da.detattn_bwd_plan(1, 32, 8192, 128, True, sched, grid=256, **ask)
-    assert (p["ring"], p["rings"], p["cooperative"], p["dq_mode"]) == (32, 8, 1, da.DQ_MODES["xcd_local"])
+    assert (p["ring"], p["rings"], p["cooperative"], p["dq_mode"]) == (32, 8, 0, da.DQ_MODES["xcd_local"])
     if sched == "atomic_nondet":
         p = da.detattn_bwd_plan(1, 32, 8192, 128, True, sched, grid=256)
         assert (p["ring"], p["cooperative"], p["dq_mode"]) == (0, 0, 0)
     p = da.detattn_bwd_plan(1, 32, 8192, 128, True, sched, grid=100)       # no XCD placement: ticket
     device_mode = 0 if sched == "atomic_nondet" else da.DQ_MODES["atomic"]
     assert (p["ring"], p["cooperative"], p["dq_mode"]) == (0, 0, device_mode)
-    p = da.detattn_bwd_plan(1, 32, 8192, 128, True, sched, grid=256, dispatch="ticket")
-    assert (p["ring"], p["cooperative"]) == (0, 0)
+    p = da.detattn_bwd_plan(1, 32, 8192, 128, True, sched, grid=256, dispatch="ticket", cooperative_launch=True)
+    assert (p["ring"], p["cooperative"]) == (0, 0)  # a ticket is only taken by a running workgroup
     p = da.detattn_bwd_plan(1, 32, 8192, 128, True, sched, grid=256, dispatch="ring", ring_size=16)
-    assert (p["ring"], p["rings"], p["cooperative"]) == (16, 16, 1)
+    assert (p["ring"], p["rings"], p["cooperative"]) == (16, 16, 0)
 
 
 CASES = [(n_kv, r) for n_kv in (1, 2, 4, 6, 8, 16, 32) for r in (1, 2)]

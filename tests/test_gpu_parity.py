@@ -124,7 +124,7 @@ def test_invariance_grid_placement_delays(case):
                                                             workspace=ws, **opts)]
         plan = da.detattn_bwd_plan(B, H, S, D, causal, sched, **opts)
         variants = [dict(debug_delay_seed=12345), dict(xcd_remap=False), dict(dq_mode="atomic"),
-                    dict(dq_mode="rmw")]
+                    dict(dq_mode="rmw"), dict(cooperative_launch=True)]
         if sched in ("serial_ascending", "descending_q"):
             # static rings instead of the ticket counter: the same order (rank = KV tile), so the
             # same add mechanism gives the same bits
@@ -154,6 +154,33 @@ def test_invariance_grid_placement_delays(case):
             else:
                 # same order, another add mechanism (VALU add vs fp32 atomic): equal up to rounding of denormals
                 assert rel_err(got[0].float().cpu().numpy(), base[0].float().cpu().numpy()) <= 1e-2
+
+
+def test_plain_ring_launch_refuses_a_grid_beyond_residency():
+    """Ring dispatch launched plainly needs the whole grid resident at once: an
+    explicit grid larger than compute units x occupancy is refused before any
+    kernel runs (the outputs keep what the caller put there)."""
+    B, H, S, D = 4, 32, 1024, 128
+    _, (q, k, v, do, o, lse) = inputs(B, H, S, D, 71, True)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    plan = da.detattn_bwd_plan(B, H, S, D, True, "symmetric_shift", grid=4 * cus)
+    assert plan["ring"] > 0 and plan["grid"] > cus and plan["cooperative"] == 0
+    ws = da.alloc_workspace(B, H, S, D)
+    out = tuple(torch.full_like(q, 7.0) for _ in range(3))
+    say(f"[residency] plan {plan}")
+    with pytest.raises(da.DetAttnError) as ei:
+        da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=True, schedule="symmetric_shift", workspace=ws,
+                                  out=out, grid=4 * cus)
+    assert "UNSUPPORTED" in str(ei.value)
+    torch.cuda.synchronize()
+    assert all(bool(torch.all(t == 7.0)) for t in out)
+    # the default grid fits, plainly and cooperatively, with the same bits
+    a = [t.clone() for t in da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=True, schedule="symmetric_shift",
+                                                      workspace=ws)]
+    b = da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=True, schedule="symmetric_shift", workspace=ws,
+                                  cooperative_launch=True)
+    assert da.detattn_device_status(ws) == 0
+    assert all(same_bits(x, y) for x, y in zip(a, b))
 
 
 @pytest.mark.parametrize("dispatch", ["ticket", "ring"])
