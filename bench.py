@@ -347,7 +347,9 @@ def main():
             f"({summ['workgroups']} WGs)")
         for name, share in summ["share"].items():
             log(f"[bench]   {share * 100:5.1f}%  {summ['ticks'][name]:8.0f}  {name}")
+        log("[bench] traced span: " + ", ".join(f"{k} {v * 100:.1f}%" for k, v in summ["span_share"].items()))
         line["trace_share"] = {k: round(v, 4) for k, v in summ["share"].items()}
+        line["trace_span_share"] = {k: round(v, 4) for k, v in summ["span_share"].items()}
         if args.trace_gantt:
             log(f"[bench] timeline of {headline} ('#' tile compute, 'w' waiting for the dQ turn, "
                 f"'e' column switch, 's' start-up (registration, first K/V), ' ' idle; one row per workgroup):")

@@ -41,6 +41,11 @@ def collect(da, tensors, causal, schedule, records=4096, **opts):
     return buf.view(plan["grid"], records, 2).cpu().numpy(), plan
 
 
+# Gantt symbols per interval (phase a -> phase b); the rest is compute ('#')
+_GANTT = {(2, 3): "w", (5, 7): "e", (7, 6): "e", (6, 0): "e", (8, 9): "s", (9, 6): "s", (8, 6): "s"}
+_PRIORITY = {" ": 0, "#": 1, "e": 2, "s": 2, "w": 3}
+
+
 def summarize(recs):
     """Mean ticks per tile of each interval, over every workgroup's complete tiles."""
     sums = {name: [] for _, _, name in INTERVALS}
@@ -77,15 +82,24 @@ def summarize(recs):
             if ph[x] == 1:
                 early += int(ph[x + 1] == 3)
                 late += int(ph[x + 1] == 2)
+    # each workgroup's traced span split into tile work, column switches
+    # (dK/dV stores, the next K/V) and start-up (registration, first K/V)
+    split = {"tiles": 0, "column switch": 0, "start-up": 0}
+    for wg in range(recs.shape[0]):
+        r = recs[wg]
+        r = r[r[:, 0] != 0]
+        t = r[:, 0].astype(np.int64)
+        ph = (r[:, 1] & 0xFF).astype(np.int64)
+        for x in range(len(r) - 1):
+            kind = _GANTT.get((int(ph[x]), int(ph[x + 1])), "#")
+            key = "column switch" if kind == "e" else "start-up" if kind == "s" else "tiles"
+            split[key] += int(t[x + 1] - t[x])
+    span_total = sum(split.values())
     return {"mean_ticks_per_tile": total, "share": {k: (v / total if total else 0.0) for k, v in out.items()},
+            "span_share": {k: (v / span_total if span_total else 0.0) for k, v in split.items()},
             "ticks": out, "workgroups": len(spans),
             "tile_period_median": float(np.median(periods)) if periods else 0.0,
             "early_turn_fraction": early / (early + late) if early + late else 0.0}
-
-
-# Gantt symbols per interval (phase a -> phase b); the rest is compute ('#')
-_GANTT = {(2, 3): "w", (5, 7): "e", (7, 6): "e", (6, 0): "e", (8, 9): "s", (9, 6): "s", (8, 6): "s"}
-_PRIORITY = {" ": 0, "#": 1, "e": 2, "s": 2, "w": 3}
 
 
 def gantt(recs, width=100, max_rows=64):
