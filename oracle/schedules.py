@@ -60,10 +60,12 @@ def items(schedule: str, mask: str, n_q: int, n_kv: int) -> List[List[Tile]]:
     atomic_nondet: ascending visits; order of dQ adds not fixed.
     shift: the SM holding KV tile j starts at its own index and wraps around,
         visiting j, j+1, ..., N-1, 0, ..., j-1 (zskr.cn section 3.2; gist.science
-        section 2.2B). With r > 1 Q tiles per KV tile the start is Q tile j*r.
+        section 2.2B). The start is Q tile j, the SM's own index, for any r (with
+        r = 1 that is the diagonal block).
     symmetric_shift: KV tiles p and n_kv-1-p form one item. Phase 1 is a shift
         over the dense lower-left rectangle (Q tiles in the bottom half, KV tiles
-        in the left half); phase 2 finishes column p above the rectangle,
+        in the left half), item p starting at the rectangle's Q tile p, its own
+        index; phase 2 finishes column p above the rectangle,
         ascending, then column n_kv-1-p, descending (zskr.cn section 3.3;
         gist.science section 2.2B). The pages give no figure of the fold; this is
         the plainest construction with one accumulator set live at a time.
@@ -82,11 +84,11 @@ def items(schedule: str, mask: str, n_q: int, n_kv: int) -> List[List[Tile]]:
             out.append([(i, j) for i in reversed(column_rows(j, n_q, r, causal))])
     elif schedule == "shift":
         for j in range(n_kv):
-            out.append([((j * r + t) % n_q, j) for t in range(n_q)])
+            out.append([((j + t) % n_q, j) for t in range(n_q)])
     elif schedule == "symmetric_shift":
         half = n_q // 2
         for p in range(n_kv // 2):
-            seq = [(half + (p * r + t) % half, p) for t in range(half)]
+            seq = [(half + (p + t) % half, p) for t in range(half)]
             seq += [(i, p) for i in range(p * r, half)]
             c = n_kv - 1 - p
             seq += [(i, c) for i in range(n_q - 1, c * r - 1, -1)]
