@@ -144,11 +144,9 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
   const int causal = mask == DETATTN_MASK_CAUSAL;
   const int n_q = s.S / bq, n_kv = s.S / bkv, r = bkv / bq;
   // AUTO: the fastest deterministic schedule measured on MI355X. Causal:
-  // symmetric shift (descending for an odd KV-tile count). Full: descending on
-  // rings of one XCD (1-6% ahead of shift there), else shift (decided below).
-  const bool auto_full = sch == DETATTN_AUTO && !causal;
+  // symmetric shift (descending for an odd KV-tile count). Full: shift.
   if (sch == DETATTN_AUTO)
-    sch = !causal ? DETATTN_DESCENDING_Q : n_kv % 2 == 0 ? DETATTN_SYMMETRIC_SHIFT : DETATTN_DESCENDING_Q;
+    sch = !causal ? DETATTN_SHIFT : n_kv % 2 == 0 ? DETATTN_SYMMETRIC_SHIFT : DETATTN_DESCENDING_Q;
   if (sch == DETATTN_SHIFT && causal) return DETATTN_ERR_UNSUPPORTED;
   if (sch == DETATTN_SYMMETRIC_SHIFT && (!causal || n_kv % 2 != 0)) return DETATTN_ERR_UNSUPPORTED;
 
@@ -200,12 +198,6 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
     if (o.dispatch == 2) ring_sched = true;
   } else if (!ring_pref) {
     ring_pref = default_ring(BH, ip);
-  }
-  if (auto_full && !ring_sched) {  // descending would fall back to the ticket counter: shift instead
-    sch = DETATTN_SHIFT;
-    sc.sch = kShift;
-    ring_sched = true;
-    ring_pref = o.ring_size ? o.ring_size : default_ring(BH, ip);
   }
   if (ring_sched) {
     // Every ring (G workgroups sharing one head's items) must be co-resident.

@@ -58,11 +58,12 @@ typedef enum { DETATTN_MASK_FULL = 0, DETATTN_MASK_CAUSAL = 1 } detattn_mask_t;
  *                    SERIAL_ASCENDING, so dQ is bit-identical to it
  *                    (explainer 3.1; summary 2.2A).
  *  SHIFT             full mask only: the workgroup holding KV tile j starts at
- *                    Q tile j*r and wraps around; dQ order = step order
- *                    (explainer 3.2; summary 2.2B).
+ *                    Q tile j, its own index, and wraps around; dQ order =
+ *                    step order (explainer 3.2; summary 2.2B).
  *  SYMMETRIC_SHIFT   causal mask only, even number of KV tiles: KV tiles p and
- *                    n-1-p share a workgroup; dense lower-left rectangle first,
- *                    then the folded triangle (explainer 3.3; summary 2.2B).
+ *                    n-1-p share a workgroup; dense lower-left rectangle first
+ *                    (item p starting at its Q tile p), then the folded
+ *                    triangle (explainer 3.3; summary 2.2B).
  *  ATOMIC_NONDET     unordered fp32 atomic adds of the dQ partials: the
  *                    non-deterministic speed reference (explainer 2.1;
  *                    summary 1). dK and dV remain deterministic.
@@ -70,9 +71,7 @@ typedef enum { DETATTN_MASK_FULL = 0, DETATTN_MASK_CAUSAL = 1 } detattn_mask_t;
  *                    for the mask (the explainer's future work, section 7,
  *                    chooses the schedule at run time): for causal masks SYMMETRIC_SHIFT
  *                    (DESCENDING_Q for an odd number of KV tiles); for full
- *                    masks DESCENDING_Q where its rings fit one XCD (1-6%
- *                    ahead of SHIFT there), else SHIFT. The choice depends
- *                    on the shape and the grid option only;
+ *                    masks SHIFT. The choice depends on the shape only;
  *                    detattn_plan_t.schedule reports it.
  */
 typedef enum {

@@ -231,12 +231,12 @@ def test_ring_option_in_plan():
 
 
 @pytest.mark.parametrize("H,S,D,causal,grid,want", [
-    (2, 4096, 128, False, 256, "descending_q"), (2, 8192, 128, True, 256, "symmetric_shift"),
-    (2, 2048, 64, True, 256, "symmetric_shift"), (16, 16384, 128, False, 256, "descending_q"),
-    (2, 4096, 128, False, 100, "shift"),                             # no ring fits one XCD
+    (2, 4096, 128, False, 256, "shift"), (2, 8192, 128, True, 256, "symmetric_shift"),
+    (2, 2048, 64, True, 256, "symmetric_shift"), (16, 16384, 128, False, 256, "shift"),
+    (2, 4096, 128, False, 100, "shift"),
     (2, 384, 128, True, 256, "descending_q"),                        # 3 KV tiles: no symmetric pairing
     (2, 192, 128, True, 256, "descending_q"),                        # 64-row KV tiles (S % 128 != 0), 3 of them
-    (2, 16384, 128, False, 256, "shift"),    # two heads: rings of one XCD would keep 64 workgroups busy
+    (2, 16384, 128, False, 256, "shift"),
 ])
 def test_auto_schedule_resolves_from_the_shape(H, S, D, causal, grid, want):
     p = da.detattn_bwd_plan(1, H, S, D, causal, "auto", grid=grid)
