@@ -126,3 +126,43 @@ def test_ring_orders_cover_each_contribution_once(n_kv, r):
                 assert sorted(js) == [j for j in range(n_kv) if S.tile_visible(i, j, r, mask == "causal")]
     with pytest.raises(ValueError):
         S.accumulation_order("shift", "full", 12, 12, ring=5)
+
+
+@pytest.mark.parametrize("bq,r", [(1, 1), (2, 1), (2, 2), (3, 2), (2, 4)])
+def test_tile_visibility_from_the_elementwise_causal_mask(bq, r):
+    """A tile pair is visible iff some key position in the KV tile is at or
+    before some query position in the Q tile (the causal mask of R3, one
+    sequence for queries and keys), counted element by element."""
+    bkv = bq * r
+    for n_kv in range(1, 6):
+        n_q = n_kv * r
+        for i in range(n_q):
+            for j in range(n_kv):
+                brute = any(kv <= q for q in range(i * bq, (i + 1) * bq) for kv in range(j * bkv, (j + 1) * bkv))
+                assert S.tile_visible(i, j, r, True) == brute, (bq, r, i, j)
+                assert S.tile_visible(i, j, r, False)
+
+
+@pytest.mark.parametrize("n_kv,r", [(4, 1), (8, 2), (6, 2), (4, 4)])
+def test_shift_items_start_at_their_own_index(n_kv, r):
+    """Each KV tile's workgroup starts at its own index and wraps around
+    (zskr.cn explainer section 3.2, read as R6 for any r): item j's first Q tile
+    is j, and the items of one step cover n_kv consecutive Q tiles (cyclically)."""
+    n_q = n_kv * r
+    its = S.items("shift", "full", n_q, n_kv)
+    for j, seq in enumerate(its):
+        assert seq[0] == (j, j)
+        assert [i for i, _ in seq] == [(j + t) % n_q for t in range(n_q)]
+    for t in range(n_q):
+        assert sorted((seq[t][0] - t) % n_q for seq in its) == list(range(n_kv))
+
+
+@pytest.mark.parametrize("n_kv,r", [(4, 1), (8, 2), (6, 2)])
+def test_symmetric_phase1_starts_at_the_items_own_index(n_kv, r):
+    """Symmetric shift's phase 1 shifts item p over the dense rectangle (Q tiles
+    n_q/2.., KV tile p) starting at the rectangle's Q tile p (R7): its first
+    n_q/2 tiles are n_q/2 + (p + t) mod n_q/2."""
+    n_q = n_kv * r
+    half = n_q // 2
+    for p, seq in enumerate(S.items("symmetric_shift", "causal", n_q, n_kv)):
+        assert seq[:half] == [(half + (p + t) % half, p) for t in range(half)]
