@@ -47,8 +47,7 @@ struct BwdArgs {
   unsigned* ticket;    // dynamic item counter
   unsigned* err;       // error bits of this call (workspace header, kHdrAbort)
   unsigned* sticky;    // error bits kept until the status is read (kHdrSticky)
-  unsigned* xcd_tab;   // XCD registration: per workgroup, 1 + the XCD it runs on
-  unsigned* xcd_arrived;  // XCD registration: workgroups registered so far
+  unsigned* xcd_tab;   // XCD registration: per workgroup, 1 + the XCD it runs on (0: not yet registered)
   int BH, S;
   float scale;
   Sched sc;
@@ -97,8 +96,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
                                                       const float* __restrict__ lse,
                                                       float* __restrict__ nlse, float* __restrict__ ndelta,
                                                       long long rows, int* flags,
-                                                      long long n_flags, unsigned* header, float* dqacc,
-                                                      long long dqacc_n4) {
+                                                      long long n_flags, unsigned* header, unsigned* xcd_tab,
+                                                      int n_tab, float* dqacc, long long dqacc_n4) {
   constexpr int TPR = D / 8;  // threads per row
   constexpr int RPB = 256 / TPR;
   const long long gtid = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -120,6 +119,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
   }
   for (long long f = gtid; f < n_flags; f += gsz) flags[f * kFlagInts] = 0;
   if (gtid < kHdrZeroWords) header[gtid] = 0;
+  for (long long x = gtid; x < n_tab; x += gsz) xcd_tab[x] = 0;  // a workgroup's entry is its arrival
   if (gtid == 0) {
     unsigned long long* tag = reinterpret_cast<unsigned long long*>(header + kHdrTag);
     if (*tag != kStickyTag) {

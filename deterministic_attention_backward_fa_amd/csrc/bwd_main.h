@@ -594,8 +594,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   // hardware's round-robin dispatch, which keeps each ring on one XCD.
   // In the XCD-local dQ modes (read-modify-write and atomics kept in one XCD's
   // L2) correctness needs that placement, so there every workgroup also
-  // registers the XCD the hardware reports (a table entry per workgroup and
-  // an arrival count, the grid being co-resident: cooperative launch), starts
+  // registers the XCD the hardware reports (a table entry per workgroup, set
+  // when it arrives; the grid is co-resident), starts
   // loading its first item under the static map, and before the item's first
   // tile checks the registered placement: rings are formed per XCD from its
   // registered workgroups in index order (floor(count / G) rings per XCD,
@@ -620,16 +620,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     if (kLocal && a.xcd_remap) {
       asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(my_xcc));
       my_xcc &= 7;
-      if (tid == 0) {
-        // relaxed device-scope atomics (no cache writeback or invalidate): the
-        // arrival increment waits, through a register dependency, for the
-        // table write to have been performed
-        const unsigned old = __hip_atomic_exchange(a.xcd_tab + wg, my_xcc + 1, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-        unsigned zero;
-        asm volatile("v_mov_b32 %0, 0 ; after %1" : "=v"(zero) : "v"(old));
-        __hip_atomic_fetch_add(a.xcd_arrived, 1u + zero, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      // the workgroup's table entry is its arrival (the preprocess cleared the
+      // table): a relaxed device-scope store, no counter that every workgroup
+      // would update in turn
+      if (tid == 0) __hip_atomic_store(a.xcd_tab + wg, my_xcc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       confirm = true;
     } else if (ring_id >= n_rings) {
       return;
@@ -644,32 +638,47 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   auto registered_ring = [&]() -> bool {
     int* sCnt = sMisc + 4;  // 8 per-XCD counts, then this workgroup's rank on its XCD
     if (tid < 9) sCnt[tid] = 0;
-    if (tid == 0) {
+    __syncthreads();
+    if (w == 0) {
+      // wave 0 reads the whole table (up to 16 entries per lane, all in
+      // flight at once) until every entry is set, then counts from those values
+      constexpr int NV = (int)WsLayout::kMaxXcdGrid / 64;
+      const int G = (int)gridDim.x;
+      unsigned v[NV];
       const long long t0 = now_ticks();
       int ok = 1;
-      while (__hip_atomic_load(a.xcd_arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gridDim.x) {
+      for (;;) {
+        bool missing = false;
+#pragma unroll
+        for (int x = 0; x < NV; ++x) {
+          const int w2 = lane + 64 * x;
+          v[x] = w2 < G ? __hip_atomic_load(a.xcd_tab + w2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1u;
+          missing |= v[x] == 0u;
+        }
+        if (__builtin_amdgcn_ballot_w64(missing) == 0) break;
         __builtin_amdgcn_s_sleep(1);
         if (now_ticks() - t0 > a.timeout_ticks ||
             __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
-          report_error(a, kErrTimeout);
+          if (lane == 0) report_error(a, kErrTimeout);
           ok = 0;
           break;
         }
       }
-      sMisc[1] = ok;
+      if (ok) {
+#pragma unroll
+        for (int x = 0; x < NV; ++x) {
+          const int w2 = lane + 64 * x;
+          const int x2 = (int)v[x] - 1;
+          if (w2 < G && x2 >= 0 && x2 < 8) {
+            atomicAdd(sCnt + x2, 1);
+            if (x2 == (int)my_xcc && w2 < (int)blockIdx.x) atomicAdd(sCnt + 8, 1);
+          }
+        }
+      }
+      if (lane == 0) sMisc[1] = ok;
     }
     __syncthreads();
     const bool ok = __builtin_amdgcn_readfirstlane(sMisc[1]) != 0;
-    if (ok) {
-      for (int w2 = tid; w2 < (int)gridDim.x; w2 += kThreads) {
-        const int x2 = (int)__hip_atomic_load(a.xcd_tab + w2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - 1;
-        if (x2 >= 0 && x2 < 8) {
-          atomicAdd(sCnt + x2, 1);
-          if (x2 == (int)my_xcc && w2 < (int)blockIdx.x) atomicAdd(sCnt + 8, 1);
-        }
-      }
-    }
-    __syncthreads();
     const int prev_ring = ring_id, prev_slot = slot, prev_n = n_rings;
     ring_id = -1;
     n_rings = 0;

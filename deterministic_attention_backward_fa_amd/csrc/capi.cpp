@@ -339,9 +339,12 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
   const long long elems = rows * s.D;
   const bool unordered = P.dqm_internal == kDqUnordered || P.dqm_internal == kDqUnorderedLocal;
 
+  // the XCD registration table is cleared for the rings of one XCD that register
+  const int n_tab = (P.pub.ring > 0 && P.xcd) ? P.pub.grid : 0;
   hipError_t e = launch_pre(s.D, static_cast<const __bf16*>(o), static_cast<const __bf16*>(dout), lse,
-                            nlse, ndelta, rows, flags,
-                            BH * P.pub.n_q, header, unordered ? dqacc : nullptr, elems, st_);
+                            nlse, ndelta, rows, flags, BH * P.pub.n_q, header,
+                            reinterpret_cast<unsigned*>(ws + L.xcdtab_off), n_tab, unordered ? dqacc : nullptr,
+                            elems, st_);
   if (e != hipSuccess) return DETATTN_ERR_HIP;
   MainLaunch M;
   std::memset(&M, 0, sizeof(M));
@@ -360,7 +363,6 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
   a.err = header + kHdrAbort;
   a.sticky = header + kHdrSticky;
   a.xcd_tab = reinterpret_cast<unsigned*>(ws + L.xcdtab_off);
-  a.xcd_arrived = header + kHdrXcdArrived;
   a.BH = (int)BH;
   a.S = s.S;
   a.scale = s.softmax_scale;

@@ -160,14 +160,11 @@ __device__ __forceinline__ void wait_vm_all() {
 //   kHdrTicket      dynamic item counter of the ticket dispatch
 //   kHdrAbort       error bits of the current call: a wait that sees it set
 //                   gives up at once, so a failing call drains quickly
-//   kHdrXcdArrived  workgroups that registered their XCD so far (XCD-local
-//                   rings; the table of registered XCDs follows the header)
 //   kHdrSticky      error bits of every call since the status was last read
 //                   (detattn_device_status reads and clears them)
 //   kHdrTag         two words: kStickyTag once the sticky word was initialised
 static constexpr int kHdrTicket = 0;
 static constexpr int kHdrAbort = 16;
-static constexpr int kHdrXcdArrived = 32;
 static constexpr int kHdrZeroWords = 48;
 static constexpr int kHdrSticky = 48;
 static constexpr int kHdrTag = 50;

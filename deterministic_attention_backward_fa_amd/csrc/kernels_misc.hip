@@ -60,17 +60,19 @@ static int grid_for(long long work_items, int per_block, int cap) {
 hipError_t launch_pre(int D, const __bf16* o, const __bf16* dout, const float* lse, float* nlse,
                       float* ndelta,
                       long long rows, int* flags,
-                      long long n_flags, unsigned* header, float* dqacc, long long dqacc_elems, hipStream_t st) {
+                      long long n_flags, unsigned* header, unsigned* xcd_tab, int n_tab, float* dqacc,
+                      long long dqacc_elems, hipStream_t st) {
   const int rpb = 256 / (D / 8);
   long long g = (rows + rpb - 1) / rpb;
   if (g < 1) g = 1;
   // the same grid also zeroes the flags and (unordered mode) the accumulator with grid-stride loops
   const long long dq4 = dqacc ? dqacc_elems / 4 : 0;
   if (D == 64)
-    bwd_pre_kernel<64><<<dim3((unsigned)g), dim3(256), 0, st>>>(o, dout, lse, nlse, ndelta, rows, flags, n_flags, header, dqacc, dq4);
+    bwd_pre_kernel<64><<<dim3((unsigned)g), dim3(256), 0, st>>>(o, dout, lse, nlse, ndelta, rows, flags, n_flags, header,
+                                                                xcd_tab, n_tab, dqacc, dq4);
   else
     bwd_pre_kernel<128><<<dim3((unsigned)g), dim3(256), 0, st>>>(o, dout, lse, nlse, ndelta, rows, flags, n_flags, header,
-                                                                 dqacc, dq4);
+                                                                 xcd_tab, n_tab, dqacc, dq4);
   return hipGetLastError();
 }
 

@@ -43,7 +43,8 @@ inline MainInfo main_info(int D, int BQ, int BKV, int causal, int dq_mode, bool 
 hipError_t launch_pre(int D, const __bf16* o, const __bf16* dout, const float* lse, float* nlse,
                       float* ndelta,
                       long long rows, int* flags,
-                      long long n_flags, unsigned* header, float* dqacc, long long dqacc_elems, hipStream_t st);
+                      long long n_flags, unsigned* header, unsigned* xcd_tab, int n_tab, float* dqacc,
+                      long long dqacc_elems, hipStream_t st);
 // fragment_order: the accumulator layout of the read-modify-write dQ modes
 // (dqacc_index); otherwise row-major (atomic modes)
 hipError_t launch_convert(int D, const float* acc, __bf16* dq, long long rows, float scale, bool fragment_order,
