@@ -90,6 +90,8 @@ def summarize(recs):
         r = r[r[:, 0] != 0]
         t = r[:, 0].astype(np.int64)
         ph = (r[:, 1] & 0xFF).astype(np.int64)
+        if not np.any(ph == 0):
+            continue  # no ring: the workgroup only registered
         for x in range(len(r) - 1):
             kind = _GANTT.get((int(ph[x]), int(ph[x + 1])), "#")
             key = "column switch" if kind == "e" else "start-up" if kind == "s" else "tiles"
@@ -110,7 +112,9 @@ def gantt(recs, width=100, max_rows=64):
     The cycle counters of different compute units are not synchronized, so
     every row starts at its workgroup's first record: the workgroups of the
     persistent grid all start at launch, up to the launch skew."""
-    rows = [wg for wg in range(recs.shape[0]) if int(np.sum(recs[wg][:, 0] != 0)) > 1][:max_rows]
+    # workgroups that ran at least one tile (those without a ring only register)
+    rows = [wg for wg in range(recs.shape[0])
+            if np.any((recs[wg][:, 0] != 0) & ((recs[wg][:, 1] & 0xFF) == 0))][:max_rows]
     if not rows:
         return ""
     spans = []
