@@ -79,7 +79,7 @@
 #define DETATTN_PF 4
 #endif
 #ifndef DETATTN_ELEM_DELAY
-#define DETATTN_ELEM_DELAY 1
+#define DETATTN_ELEM_DELAY 2
 #endif
 #ifndef DETATTN_DMA_SPAN
 #define DETATTN_DMA_SPAN 4
@@ -94,7 +94,7 @@
 #define DETATTN_DECIDE_AT 2
 #endif
 #ifndef DETATTN_LD_SPAN
-#define DETATTN_LD_SPAN 0
+#define DETATTN_LD_SPAN 7
 #endif
 #ifndef DETATTN_ST_AT
 #define DETATTN_ST_AT 0
