@@ -125,7 +125,11 @@ def warm_up(da, torch, tensors, shape, causal, sched, calls, **opts):
     torch.cuda.synchronize()
 
 
-def time_schedule(da, torch, ev, tensors, shape, causal, sched, steps, warmup, **opts):
+def time_schedule(da, torch, ev, tensors, shape, causal, sched, steps, warmup, cold=False, **opts):
+    """Warm (default): `steps` back-to-back calls between two events. Cold: before
+    each call 512 MiB of scratch is overwritten, so no input or workspace byte
+    is left in L2 or the Infinity Cache; each call is timed on its own (the
+    overwrite is outside the timed events)."""
     q, k, v, o, do, lse = tensors
     B, H, S, D = shape
     ws = da.alloc_workspace(B, H, S, D)
@@ -136,16 +140,25 @@ def time_schedule(da, torch, ev, tensors, shape, causal, sched, steps, warmup, *
     ref = [t.clone() for t in out]
     begins = [ev.create() for _ in range(steps)]
     ends = [ev.create() for _ in range(steps)]
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=q.device) if cold else None
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    per_call = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)] \
+        if cold else []
     torch.cuda.synchronize()
     t0.record()
     for s in range(steps):
+        if cold:
+            flush.fill_(s & 255)
+            per_call[s][0].record()
         da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule=sched, workspace=ws, out=out,
                                   main_begin_event=begins[s], main_end_event=ends[s], **opts)
+        if cold:
+            per_call[s][1].record()
     t1.record()
     torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
+    total_ms = sum(a.elapsed_time(b) for a, b in per_call) if cold else t0.elapsed_time(t1)
+    del flush
     main_ms = [ev.elapsed_ms(b, e) for b, e in zip(begins, ends)]
     for e in begins + ends:
         ev.destroy(e)
@@ -216,6 +229,9 @@ def main():
                     help="workgroups per ring of the shift schedules (0 = library default)")
     ap.add_argument("--pair-columns", action="store_true",
                     help="symmetric shift with both columns of a pair item resident in registers (D = 64, 64x64 tiles)")
+    ap.add_argument("--cold", action="store_true",
+                    help="overwrite 512 MiB between timed calls (no input left in L2 or the Infinity Cache); "
+                         "each call timed on its own")
     ap.add_argument("--cooperative-launch", action="store_true",
                     help="ring dispatch through HIP's cooperative launch instead of a plain launch")
     ap.add_argument("--trace", action="store_true", help="log the headline schedule's per-tile phase breakdown")
@@ -306,7 +322,8 @@ def main():
     for sched in scheds:
         log(f"[bench] timing {sched}: warmup {args.warmup}, steps {args.steps}")
         opts = sched_opts(sched)
-        r = time_schedule(da, torch, ev, tensors, (B, H, S, D), causal, sched, args.steps, args.warmup, **opts)
+        r = time_schedule(da, torch, ev, tensors, (B, H, S, D), causal, sched, args.steps, args.warmup,
+                          cold=args.cold, **opts)
         r["tflops"] = flops / (r["ms_per_step"] * 1e-3) / 1e12
         results[sched] = r
         log(f"[bench] {sched}: {r['ms_per_step']:.3f} ms/step, main {r['main_ms']:.3f} ms, "
@@ -318,7 +335,7 @@ def main():
     algo_flops = 10.0 * plan["block_q"] * plan["block_kv"] * D * tiles
     achieved = algo_flops / (head["main_ms"] * 1e-3) / 1e12
     atomic = results.get("atomic_nondet")
-    traffic = profiled_traffic(args.config) if not plan_opts else None  # the record is for the default plan
+    traffic = profiled_traffic(args.config) if not plan_opts and not args.cold else None  # taken warm, default plan
     line = {
         "metric": "deterministic attn-bwd TFLOP/s (bf16, full+causal) and ratio vs atomic nondet",
         "value": round(head["tflops"], 2),
@@ -334,7 +351,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{'causal' if causal else 'full'} attention backward B={B} H={H} S={S} D={D}",
                    "schedule": headline, "block_q": plan["block_q"], "block_kv": plan["block_kv"],
-                   "grid": plan["grid"], "ring": plan["ring"], "parallelism": "single GPU"},
+                   "grid": plan["grid"], "ring": plan["ring"], "parallelism": "single GPU",
+                   "caches": "cold (512 MiB overwritten before each call)" if args.cold else "warm"},
         "ratio_vs_atomic": round(head["tflops"] / atomic["tflops"], 4) if atomic else None,
         "ratio_vs_atomic_note": ("the atomic reference is bound by device-scope fp32 atomic adds (about 1.35 TB/s "
                                  "of dQ partials), so this ratio says little about the cost of ordering; "
@@ -375,7 +393,7 @@ def main():
     default_run = (not args.shape and args.config == "causal_b1_h32_s8192_d128" and not args.only_headline
                    and not tile_opts and not args.ring_size and args.dispatch == "default"
                    and args.dq_mode == "default" and not args.schedule and not args.pair_columns
-                   and not args.cooperative_launch)
+                   and not args.cooperative_launch and not args.cold)
     if default_run and not args.no_companion:
         cB, cH, cS, cD, ccausal, cseed = CONFIGS["full_b2_h32_s4096_d128"]
         log(f"[bench] companion full_b2_h32_s4096_d128: generating inputs (seed {cseed})")
