@@ -42,7 +42,7 @@ class BwdOptions(ctypes.Structure):
                 ("main_begin_event", ctypes.c_void_p), ("main_end_event", ctypes.c_void_p),
                 ("trace", ctypes.c_void_p), ("trace_records", ctypes.c_int32), ("ring_size", ctypes.c_int32),
                 ("dispatch", ctypes.c_int32), ("pair_columns", ctypes.c_int32),
-                ("cooperative_launch", ctypes.c_int32)]
+                ("cooperative_launch", ctypes.c_int32), ("debug_misplace", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -133,12 +133,13 @@ def _check_tensor(name, t, dtype, shape):
 
 def _options(block_q=0, block_kv=0, grid=0, xcd_remap=None, dq_mode="default", debug_delay_seed=0, timeout_us=0,
              debug_skip_signal=0, main_begin_event=None, main_end_event=None, trace=None, trace_records=0,
-             ring_size=0, dispatch="default", pair_columns=False, cooperative_launch=False):
+             ring_size=0, dispatch="default", pair_columns=False, cooperative_launch=False, debug_misplace=False):
     xr = 0 if xcd_remap is None else (1 if xcd_remap else 2)
     return BwdOptions(int(block_q), int(block_kv), int(grid), xr, DQ_MODES[dq_mode], int(debug_delay_seed),
                       int(timeout_us), int(debug_skip_signal), main_begin_event, main_end_event,
                       trace.data_ptr() if trace is not None else None, int(trace_records), int(ring_size),
-                      DISPATCH[dispatch], 1 if pair_columns else 0, 1 if cooperative_launch else 0)
+                      DISPATCH[dispatch], 1 if pair_columns else 0, 1 if cooperative_launch else 0,
+                      1 if debug_misplace else 0)
 
 
 def detattn_fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
@@ -179,7 +180,7 @@ def attn_bwd_deterministic(q, k, v, o, dout, lse, causal=False, schedule="serial
                            workspace=None, out=None, stream=None, check=False, **opts):
     """dQ, dK, dV (bf16) of softmax attention. `opts` are BwdOptions fields
     (block_q, block_kv, grid, xcd_remap, dq_mode, debug_delay_seed, timeout_us, debug_skip_signal, ring_size, dispatch,
-    pair_columns, cooperative_launch).
+    pair_columns, cooperative_launch, debug_misplace).
     check=True synchronises the stream after the call and raises DetAttnError if the
     workspace's device status reports an error (detattn_device_status)."""
     B, H, S, D = q.shape

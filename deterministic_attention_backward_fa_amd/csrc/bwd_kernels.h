@@ -58,6 +58,7 @@ struct BwdArgs {
   long long timeout_ticks;  // s_memrealtime ticks (100 MHz)
   unsigned delay_seed;
   int skip_item;       // testing: global item index whose first signal is withheld, or -1
+  int misplace;        // testing: XCD-local rings start from a wrong guess (workgroup w takes w+1's place)
   unsigned long long* trace;  // optional per-workgroup phase timestamps
   int trace_records;
 };

@@ -609,8 +609,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   unsigned my_xcc = 0;
   if (!a.ticket_mode) {
     const int wg = blockIdx.x;
+    // the static map's guess (testing: shifted by one workgroup, so that the
+    // registered placement differs and every workgroup takes the restart path)
+    const int wg_map = (kLocal && a.xcd_remap && a.misplace) ? (wg + 1) % (int)gridDim.x : wg;
     if (a.xcd_remap) {
-      const int x = wg & 7, u = wg >> 3;
+      const int x = wg_map & 7, u = wg_map >> 3;
       ring_id = (u / a.ring) * 8 + x;
       slot = u % a.ring;
     } else {

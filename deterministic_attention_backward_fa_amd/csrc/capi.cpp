@@ -133,7 +133,8 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
   if (opt) o = *opt;
   if (o.block_q < 0 || o.block_kv < 0 || o.grid < 0 || o.xcd_remap < 0 || o.xcd_remap > 2 || o.dq_mode < 0 ||
       o.dq_mode > 3 || o.ring_size < 0 || o.dispatch < 0 || o.dispatch > 2 || o.pair_columns < 0 ||
-      o.pair_columns > 1 || o.cooperative_launch < 0 || o.cooperative_launch > 1)
+      o.pair_columns > 1 || o.cooperative_launch < 0 || o.cooperative_launch > 1 || o.debug_misplace < 0 ||
+      o.debug_misplace > 1)
     return DETATTN_ERR_INVALID_ARG;
   int bq, bkv;
   default_tiles(s.D, s.S, bq, bkv);
@@ -379,6 +380,7 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
   a.timeout_ticks = P.timeout_ticks;
   a.delay_seed = options ? options->debug_delay_seed : 0u;
   a.skip_item = (options && options->debug_skip_signal > 0) ? options->debug_skip_signal - 1 : -1;
+  a.misplace = options ? options->debug_misplace : 0;
   if (options && options->trace) {
     a.trace = reinterpret_cast<unsigned long long*>(options->trace);
     a.trace_records = options->trace_records;

@@ -165,6 +165,10 @@ typedef struct {
                                 device, at about 15 us of added launch latency per call. Ticket dispatch
                                 needs neither (a ticket is only taken by a running workgroup) and always
                                 launches plainly. */
+  int32_t debug_misplace;    /* testing: 1 = rings of one XCD start from a wrong guess of where each workgroup
+                                runs (workgroup w assumes w+1's place), so the placement the hardware reports
+                                differs and every workgroup drops its first loads and takes its registered
+                                ring; results must not change. No effect elsewhere. */
 } detattn_bwd_options_t;
 
 /* Phase ids written into the optional trace (low 8 bits of the second word). */

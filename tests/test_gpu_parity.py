@@ -156,6 +156,37 @@ def test_invariance_grid_placement_delays(case):
                 assert rel_err(got[0].float().cpu().numpy(), base[0].float().cpu().numpy()) <= 1e-2
 
 
+MISPLACE_CASES = [
+    # (B, H, S, D, causal, seed, schedule): XCD-local rings by default
+    (2, 16, 1024, 64, True, 81, "symmetric_shift"),
+    (1, 32, 2048, 128, True, 82, "symmetric_shift"),
+    (2, 16, 1024, 128, False, 83, "shift"),
+    (2, 16, 2048, 128, False, 84, "descending_q"),
+]
+
+
+@pytest.mark.parametrize("case", MISPLACE_CASES, ids=lambda c: f"B{c[0]}H{c[1]}S{c[2]}D{c[3]}{'c' if c[4] else 'f'}-{c[6]}")
+def test_wrong_placement_guess_changes_no_bit(case):
+    """Rings of one XCD are formed from the XCD each workgroup reports. With
+    the static guess shifted by one workgroup (debug_misplace), the registered
+    placement differs from the guess for the workgroups, which drop their first
+    loads and start over on their registered ring: the outputs are the same
+    bits as with the right guess, and the call reports no error."""
+    B, H, S, D, causal, seed, sched = case
+    _, (q, k, v, do, o, lse) = inputs(B, H, S, D, seed, causal)
+    plan = da.detattn_bwd_plan(B, H, S, D, causal, sched)
+    assert plan["ring"] > 0 and plan["dq_mode"] == da.DQ_MODES["xcd_local"], plan
+    ws = da.alloc_workspace(B, H, S, D)
+    say(f"[misplace] {case} plan {plan}")
+    base = [t.clone() for t in da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule=sched,
+                                                        workspace=ws)]
+    for _ in range(3):
+        got = da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule=sched, workspace=ws,
+                                        debug_misplace=True)
+        assert da.detattn_device_status(ws) == 0
+        assert all(same_bits(a_, b_) for a_, b_ in zip(base, got))
+
+
 def test_plain_ring_launch_refuses_a_grid_beyond_residency():
     """Ring dispatch launched plainly needs the whole grid resident at once: an
     explicit grid larger than compute units x occupancy is refused before any
