@@ -13,7 +13,6 @@ times (both masks) and the fitted model is compared with each measurement; the
 printed table (pytest -s) is the study's record. The model must rank the causal
 schedules as the hardware does and predict every time within 35%.
 """
-import math
 
 import pytest
 import torch
