@@ -2,8 +2,11 @@
 
 For every workload shape below, every valid schedule runs with the library's
 default plan (tiles, grid, rings, dQ mode). The fp64 oracle computes sampled
-outputs one by one on two heads (the first and the last): dQ at sampled query
-rows, dK and dV at sampled key rows, plus every row's log-sum-exp. The bar is
+outputs one by one on three heads (the first, a middle and the last; two at
+64k tokens): dQ at sampled query rows, dK and dV at sampled key rows (32 random
+positions each, plus the first and last and the positions around 64- and
+128-row tile edges and the sequence's midpoint, where symmetric shift's
+rectangle starts), plus every row's log-sum-exp. The bar is
 the same as for the small cases, max|gpu - oracle| <= 2e-2 * max|oracle| over
 the sampled values, and the bitwise relations between schedules that share an
 accumulation order hold at full size. Every deterministic schedule of the
@@ -55,9 +58,10 @@ def test_fullsize_sampled_parity_and_determinism(name):
     q, k, v, do = (t.cuda() for t in cpu)
     o, lse = da.detattn_fwd(q, k, v, causal=causal)
     torch.cuda.synchronize()
-    rows = sample_indices(S, 12, seed)
-    cols = sample_indices(S, 12, seed + 1)
-    heads = [(0, 0), (B - 1, H - 1)]
+    edges = {63, 64, 127, 128, S // 2 - 1, S // 2, S - 65, S - 64}
+    rows = sorted(set(sample_indices(S, 32, seed)) | {x for x in edges if 0 <= x < S})
+    cols = sorted(set(sample_indices(S, 32, seed + 1)) | {x for x in edges if 0 <= x < S})
+    heads = [(0, 0), (B // 2, H // 2), (B - 1, H - 1)] if S <= 16384 else [(0, 0), (B - 1, H - 1)]
     refs = {}
     for (b, h) in heads:
         say(f"[fullsize] {name}: oracle head ({b},{h})")
