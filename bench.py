@@ -162,8 +162,14 @@ def time_schedule(da, torch, ev, tensors, shape, causal, sched, steps, warmup, c
     main_ms = [ev.elapsed_ms(b, e) for b, e in zip(begins, ends)]
     for e in begins + ends:
         ev.destroy(e)
-    status = da.detattn_device_status(ws)
+    # bit equality of every timed call's outputs can only be seen at the end of
+    # the timed loop (one set of output buffers); up to 10 further calls, untimed,
+    # are each compared with the first warm-up result
     same = all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(ref, out))
+    for _ in range(min(steps, 10)):
+        da.attn_bwd_deterministic(q, k, v, o, do, lse, causal=causal, schedule=sched, workspace=ws, out=out, **opts)
+        same = same and all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(ref, out))
+    status = da.detattn_device_status(ws)
     srt = sorted(main_ms)
     return {"ms_per_step": total_ms / steps, "main_ms": sum(main_ms) / steps,
             "main_ms_median": srt[len(srt) // 2] if len(srt) % 2 else 0.5 * (srt[len(srt) // 2 - 1] + srt[len(srt) // 2]),
