@@ -146,12 +146,13 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
   const int n_q = s.S / bq, n_kv = s.S / bkv, r = bkv / bq;
   // AUTO: the fastest deterministic schedule measured on MI355X. Full:
   // shift. Causal: symmetric shift, except descending for an odd KV-tile
-  // count and, at D = 128, from 64 KV tiles on (several rounds of items per
-  // ring, where descending's snake order measured 0-4% ahead).
+  // count and, at D = 128, from 128 KV tiles on (several rounds of items per
+  // ring, where descending's snake order measured 1-3% ahead; at 64 KV tiles
+  // the two measured within 2% of each other either way).
   if (sch == DETATTN_AUTO)
     sch = !causal                          ? DETATTN_SHIFT
           : n_kv % 2 != 0                  ? DETATTN_DESCENDING_Q
-          : (s.D == 128 && n_kv >= 64)     ? DETATTN_DESCENDING_Q
+          : (s.D == 128 && n_kv >= 128)    ? DETATTN_DESCENDING_Q
                                            : DETATTN_SYMMETRIC_SHIFT;
   if (sch == DETATTN_SHIFT && causal) return DETATTN_ERR_UNSUPPORTED;
   if (sch == DETATTN_SYMMETRIC_SHIFT && (!causal || n_kv % 2 != 0)) return DETATTN_ERR_UNSUPPORTED;

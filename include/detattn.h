@@ -71,7 +71,7 @@ typedef enum { DETATTN_MASK_FULL = 0, DETATTN_MASK_CAUSAL = 1 } detattn_mask_t;
  *                    for the mask (the explainer's future work, section 7,
  *                    chooses the schedule at run time): for causal masks SYMMETRIC_SHIFT,
  *                    except DESCENDING_Q for an odd number of KV tiles and,
- *                    at D = 128, from 64 KV tiles on; for full masks SHIFT.
+ *                    at D = 128, from 128 KV tiles on; for full masks SHIFT.
  *                    The choice depends on the shape only;
  *                    detattn_plan_t.schedule reports it.
  */

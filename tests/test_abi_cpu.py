@@ -231,7 +231,8 @@ def test_ring_option_in_plan():
 
 
 @pytest.mark.parametrize("H,S,D,causal,grid,want", [
-    (2, 4096, 128, False, 256, "shift"), (2, 8192, 128, True, 256, "descending_q"),
+    (2, 4096, 128, False, 256, "shift"), (2, 8192, 128, True, 256, "symmetric_shift"),
+    (2, 16384, 128, True, 256, "descending_q"),
     (2, 4096, 128, True, 256, "symmetric_shift"), (2, 8192, 64, True, 256, "symmetric_shift"),
     (2, 2048, 64, True, 256, "symmetric_shift"), (16, 16384, 128, False, 256, "shift"),
     (2, 4096, 128, False, 100, "shift"),
