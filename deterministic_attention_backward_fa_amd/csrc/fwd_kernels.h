@@ -5,7 +5,8 @@
 // A workgroup of 4 waves owns 128 query rows (32 per wave, kept in registers)
 // and streams KV tiles of 64 rows through LDS. At D = 64 the next tile's K, V
 // are loaded into registers while the current one is computed (at D = 128 the
-// extra registers cost more occupancy than the overlap gains). The D = 128
+// extra registers cost more occupancy than the overlap gains; there the tile
+// goes straight from global memory to LDS by LDS-DMA). The D = 128
 // instances are held to 168 registers, three waves per SIMD, and the D = 64
 // ones to 128, four waves (the causal instances spill a few registers there
 // and are still faster than with fewer waves). Under a causal mask the grid
@@ -33,6 +34,12 @@ struct FwdCfg {
   static constexpr int NPT = BKV * CPR / 256;    // chunks per thread per tile
   static_assert(NPT * 256 == BKV * CPR, "tile chunks split evenly over 256 threads");
   static constexpr bool PREFETCH = D <= 64;     // K, V of the next tile in registers
+  static constexpr bool DMA = !PREFETCH;        // else K, V go through LDS-DMA
+  // LDS-DMA of a tile: 16-byte chunks in padded-row order (D / 8 data chunks
+  // and one padding chunk per row, P * 2 bytes), 1 KB per instruction
+  static constexpr int NCH = D / 8;
+  static constexpr int DMA_INS = BKV * (NCH + 1) / 64;
+  static_assert(BKV * (NCH + 1) % 64 == 0 && P * 2 == (NCH + 1) * 16, "DMA tile layout");
 };
 
 template <int D, bool CAUSAL>
@@ -72,15 +79,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 
       vr[x] = *reinterpret_cast<const bf16x8*>(v + head + (long long)(kv + r) * D + 8 * c);
     }
   };
+  // LDS-DMA: instruction ins moves chunks 64 ins .. + 63 of the padded tile
+  // (row p / (NCH + 1), chunk p % (NCH + 1)); a padding chunk re-reads its
+  // row's first chunk, whose bytes land in the padding and are never read
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  auto dma_tile = [&](int kv) {
+    const unsigned char* gk = reinterpret_cast<const unsigned char*>(k + head + (long long)kv * D);
+    const unsigned char* gv = reinterpret_cast<const unsigned char*>(v + head + (long long)kv * D);
+    for (int ins = wu; ins < C::DMA_INS; ins += 4) {
+      const int p = ins * 64 + lane, row = p / (C::NCH + 1), col = p % (C::NCH + 1);
+      const int go = row * D * 2 + (col < C::NCH ? col : 0) * 16;
+      __builtin_amdgcn_global_load_lds((gbl_void*)(gk + go), (lds_void*)(reinterpret_cast<unsigned char*>(sK) + ins * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_void*)(gv + go), (lds_void*)(reinterpret_cast<unsigned char*>(sV) + ins * 1024), 16, 0, 0);
+    }
+  };
   if constexpr (C::PREFETCH) load_tile(0);
   for (int kv0 = 0; kv0 < kv_end; kv0 += C::BKV) {
     __syncthreads();  // every wave is done with the previous tile in LDS
-    if constexpr (!C::PREFETCH) load_tile(kv0);
+    if constexpr (C::DMA) {
+      dma_tile(kv0);  // complete at the barrier below (it waits for every vector-memory operation)
+    } else {
+      // the tile prefetched into registers during the previous one
 #pragma unroll
-    for (int x = 0; x < C::NPT; ++x) {
-      const int cidx = tid + 256 * x, r = cidx / C::CPR, c = cidx % C::CPR;
-      lds_store16(sK + r * C::P + 8 * c, kr[x]);
-      lds_store16(sV + r * C::P + 8 * c, vr[x]);
+      for (int x = 0; x < C::NPT; ++x) {
+        const int cidx = tid + 256 * x, r = cidx / C::CPR, c = cidx % C::CPR;
+        lds_store16(sK + r * C::P + 8 * c, kr[x]);
+        lds_store16(sV + r * C::P + 8 * c, vr[x]);
+      }
     }
     __syncthreads();
     if constexpr (C::PREFETCH) {
