@@ -316,7 +316,6 @@ __device__ __forceinline__ u32x2 lds_tr_agpr(uint32_t addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=a"(r) : "v"(addr), "i"(OFF));
   return r;
 }
-__device__ __forceinline__ void lgkm_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 template <int N>
 __device__ __forceinline__ void lgkm_wait(u32x4& x) {
   static_assert(N >= 0 && N <= 15, "lgkmcnt field");
@@ -363,8 +362,6 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
-// Wait until at most N vector-memory operations of this wave are in flight
-// (they complete in issue order), then barrier.
 // 16-byte buffer read (per lane: voff + OFF bytes past the resource base plus
 // soff), issued outside the compiler's wait tracking: the caller waits with
 // vm_wait_tied. SC1 selects coherence across XCDs, else within the XCD (sc0).
@@ -389,13 +386,6 @@ template <int N>
 __device__ __forceinline__ void vm_wait() {
   static_assert(N >= 0 && N <= 63, "vmcnt field");
   asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void vm_barrier() {
-  static_assert(N >= 0 && N <= 63, "vmcnt field");
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"i"(N) : "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& x) { return __builtin_bit_cast(bf16x8, x); }
 // keep a value in accumulation registers (AGPRs): MFMA-only operands live

@@ -50,11 +50,6 @@ static constexpr int kBufSc1 = 16;
 // blocks, each block as D/32 column blocks of 32 x 32; inside such a block the
 // element (row 8h + 4g + e, column c) sits at float (h * 64 + 32g + c) * 4 + e,
 // so one lane's four accumulator registers 4h .. 4h+3 are 16 contiguous bytes.
-__host__ __device__ __forceinline__ long long dqacc_index(long long row, int col, int D) {
-  const long long blk = (row >> 5) * (D >> 5) + (col >> 5);
-  const int rr = (int)(row & 31), h = rr >> 3, g = (rr >> 2) & 1, e = rr & 3;
-  return blk * 1024 + (h * 64 + 32 * g + (col & 31)) * 4 + e;
-}
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

@@ -23,7 +23,7 @@ __global__ __launch_bounds__(256) void bwd_convert_rm_kernel(const float* __rest
 }
 
 // dQ = bf16_rne(scale * acc) from an accumulator in fragment order
-// (dqacc_index): a workgroup takes 32-row blocks, reads each block's 16-byte
+// (described in common.h): a workgroup takes 32-row blocks, reads each block's 16-byte
 // runs, and writes the rows through LDS as 16-byte runs.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_convert_kernel(const float* __restrict__ acc, __bf16* __restrict__ dq,

@@ -46,7 +46,7 @@ hipError_t launch_pre(int D, const __bf16* o, const __bf16* dout, const float* l
                       long long n_flags, unsigned* header, unsigned* xcd_tab, int n_tab, float* dqacc,
                       long long dqacc_elems, hipStream_t st);
 // fragment_order: the accumulator layout of the read-modify-write dQ modes
-// (dqacc_index); otherwise row-major (atomic modes)
+// (described in common.h); otherwise row-major (atomic modes)
 hipError_t launch_convert(int D, const float* acc, __bf16* dq, long long rows, float scale, bool fragment_order,
                           hipStream_t st);
 hipError_t launch_main(const MainLaunch& L, hipStream_t st);
