@@ -55,11 +55,12 @@ namespace detattn {
 // contributions of earlier rounds and the round's own wrap-around.
 struct SegWalk {
   static constexpr int kBig = 1 << 28;
+  static constexpr int kJumped = -2;  // jump_t once the jump has been taken
   int i;                // Q tile of the current step
   int n;                // steps since the segment (or the jump) began; q = n >> rs
   int di;               // Q tile increment per step (+1 or -1)
   int wrap_at, wrap_to; // a step reaching Q tile wrap_at continues at wrap_to
-  int jump_t, jump_i;   // step jump_t continues at Q tile jump_i, n restarts at 0
+  int jump_t, jump_i;   // step jump_t continues at Q tile jump_i, n restarts at 0 (kJumped afterwards)
   int rs;               // q = n >> rs (0 where a step moves one Q tile between items, else log2(r))
   int rsi;              // log2(r): Q tile i to its row block of r tiles, i >> rsi
   int rs_jump;          // rs after the jump
@@ -75,14 +76,29 @@ struct SegWalk {
 
   __host__ __device__ __forceinline__ void advance(int t) {
     i += di;
-    if (i == wrap_at) i = wrap_to;
+    if (i == wrap_at) {
+      i = wrap_to;
+      if (jump_t == kJumped) {  // the next residue class of the run after the jump
+        ++wrap_at;
+        ++wrap_to;
+      }
+    }
     ++n;
+    if (jump_t == kJumped) n = i - jump_i;
     if (t == jump_t) {
+      // the run after the jump (symmetric shift's column above the rectangle)
+      // takes one residue class mod r after another, r rows per step: it ends
+      // each class where the rectangle begins (the phase-1 wrap target) and
+      // continues at the next class, n counting rows from the run's start
       i = jump_i;
       n = 0;
       c2 = kBig;
       e0 = -kBig;
       rs = rs_jump;
+      di = 1 << rs_jump;
+      wrap_at = wrap_to;
+      wrap_to = jump_i + 1;
+      jump_t = kJumped;
     }
   }
 };
@@ -141,8 +157,10 @@ struct Sched {
         const int t2 = t - half;
         const int top = half - p * r;  // rows p*r .. half-1 of column p
         if (t2 < top) {
+          // one residue class mod r after another, L = top / r rows each
+          const int L = top / r;
           j = p;
-          i = p * r + t2;
+          i = p * r + t2 / L + r * (t2 % L);
         } else {
           j = n_kv - 1 - p;
           i = n_q - 1 - (t2 - top);

@@ -65,10 +65,16 @@ def items(schedule: str, mask: str, n_q: int, n_kv: int) -> List[List[Tile]]:
     symmetric_shift: KV tiles p and n_kv-1-p form one item. Phase 1 is a shift
         over the dense lower-left rectangle (Q tiles in the bottom half, KV tiles
         in the left half), item p starting at the rectangle's Q tile p, its own
-        index; phase 2 finishes column p above the rectangle,
-        ascending, then column n_kv-1-p, descending (zskr.cn section 3.3;
-        gist.science section 2.2B). The pages give no figure of the fold; this is
-        the plainest construction with one accumulator set live at a time.
+        index; phase 2 finishes column p above the rectangle, then column
+        n_kv-1-p, descending (zskr.cn section 3.3; gist.science section 2.2B).
+        Column p's rows above the rectangle start at row p*r; they are taken
+        ascending one residue class mod r after another (rows p*r, p*r + r, ...,
+        then p*r + 1, p*r + 1 + r, ...), so the items of one step visit rows r
+        apart inside one class and consecutive rows of it from step to step.
+        Each dQ tile receives its partials in the same order as with plain
+        ascending rows (larger p first), so only the visit order inside an item
+        differs. The pages give no figure of the fold; this is the plainest
+        construction with one accumulator set live at a time.
     """
     causal = mask == "causal"
     r = n_q // n_kv
@@ -89,7 +95,9 @@ def items(schedule: str, mask: str, n_q: int, n_kv: int) -> List[List[Tile]]:
         half = n_q // 2
         for p in range(n_kv // 2):
             seq = [(half + (p + t) % half, p) for t in range(half)]
-            seq += [(i, p) for i in range(p * r, half)]
+            # column p above the rectangle, rows p*r .. half-1, one residue
+            # class mod r after another (r = 1: simply ascending)
+            seq += [(i, p) for k in range(r) for i in range(p * r + k, half, r)]
             c = n_kv - 1 - p
             seq += [(i, c) for i in range(n_q - 1, c * r - 1, -1)]
             out.append(seq)

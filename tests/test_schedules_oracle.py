@@ -166,3 +166,33 @@ def test_symmetric_phase1_starts_at_the_items_own_index(n_kv, r):
     half = n_q // 2
     for p, seq in enumerate(S.items("symmetric_shift", "causal", n_q, n_kv)):
         assert seq[:half] == [(half + (p + t) % half, p) for t in range(half)]
+
+
+@pytest.mark.parametrize("n_kv,r", [(4, 1), (8, 2), (6, 2), (16, 2)])
+def test_symmetric_rows_above_the_rectangle_go_by_residue_class(n_kv, r):
+    """Phase 2 of item p first takes column p's rows above the rectangle,
+    p*r .. n_q/2 - 1, one residue class mod r after another (R7), then column
+    n_kv-1-p downward. Every dQ tile then receives its partials in the same
+    order as if those rows were taken plainly upward, so the reading changes the
+    visits inside an item, not a dQ tile's accumulation order."""
+    n_q = n_kv * r
+    half = n_q // 2
+    its = S.items("symmetric_shift", "causal", n_q, n_kv)
+    plain = []
+    for p, seq in enumerate(its):
+        top = seq[half:half + half - p * r]
+        assert top == [(i, p) for k in range(r) for i in range(p * r + k, half, r)]
+        rest = seq[half + len(top):]
+        assert rest == [(i, n_kv - 1 - p) for i in range(n_q - 1, (n_kv - 1 - p) * r - 1, -1)]
+        plain.append(seq[:half] + [(i, p) for i in range(p * r, half)] + rest)
+
+    def order(items):
+        got = {}
+        for t in range(max(len(x) for x in items)):
+            for x in items:
+                if t < len(x):
+                    got.setdefault(x[t][0], []).append(x[t][1])
+        return got
+
+    assert order(its) == order(plain)
+    assert order(its) == S.accumulation_order("symmetric_shift", "causal", n_q, n_kv)
