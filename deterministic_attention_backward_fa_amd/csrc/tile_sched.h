@@ -162,8 +162,11 @@ struct Sched {
           j = p;
           i = p * r + t2 / L + r * (t2 % L);
         } else {
+          // column n_kv-1-p downward, one residue class mod r after another,
+          // L = p + 1 rows each
+          const int u = t2 - top, L = p + 1;
           j = n_kv - 1 - p;
-          i = n_q - 1 - (t2 - top);
+          i = n_q - r + u / L - r * (u % L);
         }
         return;
       }
@@ -220,10 +223,15 @@ struct Sched {
           w.c2 = half - 1 - g;
           w.rs = 0;
         } else {         // column n_kv-1-it downward from the last row, after the round's phase 1
+          // one residue class mod r after another: each class ends below row
+          // j*r and the next starts one row higher at the bottom
           j = n_kv - 1 - it;
-          w.i = n_q - 1;
-          w.di = -1;
-          w.wrap_at = -2;
+          w.i = n_q - r;
+          w.di = -r;
+          w.wrap_at = j * r - r;
+          w.wrap_to = n_q - r + 1;
+          w.jump_t = SegWalk::kJumped;  // the wrap moves on to the next class
+          w.jump_i = 0;                 // n = i >= 0 (this segment's rank is base + the row term)
           w.base = kG + 2 * Gr - 1 - g;
           w.c1 = 0;
         }

@@ -69,11 +69,12 @@ def items(schedule: str, mask: str, n_q: int, n_kv: int) -> List[List[Tile]]:
         n_kv-1-p, descending (zskr.cn section 3.3; gist.science section 2.2B).
         Column p's rows above the rectangle start at row p*r; they are taken
         ascending one residue class mod r after another (rows p*r, p*r + r, ...,
-        then p*r + 1, p*r + 1 + r, ...), so the items of one step visit rows r
-        apart inside one class and consecutive rows of it from step to step.
-        Each dQ tile receives its partials in the same order as with plain
-        ascending rows (larger p first), so only the visit order inside an item
-        differs. The pages give no figure of the fold; this is the plainest
+        then p*r + 1, p*r + 1 + r, ...), and column n_kv-1-p's rows descending
+        the same way (rows n_q - r, n_q - 2r, ..., then n_q - r + 1, ...), so
+        the items of one step stay inside one class of rows. Each dQ tile
+        receives its partials in the same order as with plain ascending and
+        descending rows (larger p first), so only the visit order inside an
+        item differs. The pages give no figure of the fold; this is the plainest
         construction with one accumulator set live at a time.
     """
     causal = mask == "causal"
@@ -99,7 +100,9 @@ def items(schedule: str, mask: str, n_q: int, n_kv: int) -> List[List[Tile]]:
             # class mod r after another (r = 1: simply ascending)
             seq += [(i, p) for k in range(r) for i in range(p * r + k, half, r)]
             c = n_kv - 1 - p
-            seq += [(i, c) for i in range(n_q - 1, c * r - 1, -1)]
+            # column c downward from the last row, likewise one residue class
+            # mod r after another (rows n_q-r, n_q-2r, ..., then n_q-r+1, ...)
+            seq += [(i, c) for k in range(r) for i in range(n_q - r + k, c * r - 1, -r)]
             out.append(seq)
     return out
 

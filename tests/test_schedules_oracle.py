@@ -170,11 +170,12 @@ def test_symmetric_phase1_starts_at_the_items_own_index(n_kv, r):
 
 @pytest.mark.parametrize("n_kv,r", [(4, 1), (8, 2), (6, 2), (16, 2)])
 def test_symmetric_rows_above_the_rectangle_go_by_residue_class(n_kv, r):
-    """Phase 2 of item p first takes column p's rows above the rectangle,
-    p*r .. n_q/2 - 1, one residue class mod r after another (R7), then column
-    n_kv-1-p downward. Every dQ tile then receives its partials in the same
-    order as if those rows were taken plainly upward, so the reading changes the
-    visits inside an item, not a dQ tile's accumulation order."""
+    """Phase 2 of item p takes column p's rows above the rectangle, p*r ..
+    n_q/2 - 1, upward one residue class mod r after another (R7), then column
+    n_kv-1-p's rows downward the same way. Every dQ tile then receives its
+    partials in the same order as if the rows were taken plainly upward and
+    downward, so the reading changes the visits inside an item, not a dQ tile's
+    accumulation order."""
     n_q = n_kv * r
     half = n_q // 2
     its = S.items("symmetric_shift", "causal", n_q, n_kv)
@@ -183,8 +184,10 @@ def test_symmetric_rows_above_the_rectangle_go_by_residue_class(n_kv, r):
         top = seq[half:half + half - p * r]
         assert top == [(i, p) for k in range(r) for i in range(p * r + k, half, r)]
         rest = seq[half + len(top):]
-        assert rest == [(i, n_kv - 1 - p) for i in range(n_q - 1, (n_kv - 1 - p) * r - 1, -1)]
-        plain.append(seq[:half] + [(i, p) for i in range(p * r, half)] + rest)
+        c = n_kv - 1 - p
+        assert rest == [(i, c) for k in range(r) for i in range(n_q - r + k, c * r - 1, -r)]
+        plain.append(seq[:half] + [(i, p) for i in range(p * r, half)] +
+                     [(i, c) for i in range(n_q - 1, c * r - 1, -1)])
 
     def order(items):
         got = {}
