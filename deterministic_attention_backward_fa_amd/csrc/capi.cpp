@@ -147,8 +147,8 @@ int make_plan(const detattn_shape_t& s, detattn_mask_t mask, detattn_schedule_t 
   // AUTO: the fastest deterministic schedule measured on MI355X. Full:
   // shift. Causal: symmetric shift, except descending for an odd KV-tile
   // count and, at D = 128, from 128 KV tiles on (several rounds of items per
-  // ring, where descending's snake order measured 1-3% ahead; at 64 KV tiles
-  // the two measured within 2% of each other either way).
+  // ring, where descending's snake order measured 0.4-2.5% ahead; at 64 KV
+  // tiles symmetric shift measured ahead).
   if (sch == DETATTN_AUTO)
     sch = !causal                          ? DETATTN_SHIFT
           : n_kv % 2 != 0                  ? DETATTN_DESCENDING_Q
