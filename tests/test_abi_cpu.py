@@ -183,7 +183,7 @@ def test_library_schedule_matches_oracle(sched, mask, n_kv, r):
             assert [c for _, _, c in got] == [ranks[t] for t in want]
 
 
-RING_CASES = [(n_kv, r) for n_kv in (4, 8, 16, 64, 128) for r in (1, 2)]
+RING_CASES = [(n_kv, r) for n_kv in (4, 6, 8, 12, 16, 64, 128) for r in (1, 2)]
 
 
 @pytest.mark.parametrize("n_kv,r", RING_CASES)
