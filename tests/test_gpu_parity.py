@@ -30,6 +30,7 @@ SMALL = [
     (1, 1, 512, 64, True, 13, {"block_q": 64, "block_kv": 128}),      # r = 2 at D = 64
     (1, 2, 512, 128, False, 14, {}),                                   # 64x128 tiles, r = 2
     (1, 2, 512, 128, True, 15, {}),
+    (1, 2, 768, 128, True, 18, {}),                                    # 6 KV tiles: 3 symmetric pairs, r = 2
     (1, 2, 256, 128, False, 16, {"block_q": 64, "block_kv": 64}),     # the long-context tile shape
     (1, 2, 256, 128, True, 17, {"block_q": 64, "block_kv": 64}),
 ]
@@ -247,6 +248,7 @@ RING_CASES = [
     (1, 2, 512, 128, True, 22, {"block_q": 64, "block_kv": 64}, (1, 2)),      # symmetric, 4 items
     (1, 2, 1024, 128, True, 23, {}, (1, 2)),                                  # symmetric, r = 2
     (1, 1, 1024, 128, False, 24, {}, (2, 4)),                                 # shift, r = 2
+    (1, 2, 1536, 128, True, 25, {}, (1, 3)),                                  # symmetric, 6 pairs, r = 2
 ]
 
 
