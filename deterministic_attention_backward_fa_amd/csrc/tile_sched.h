@@ -23,7 +23,9 @@
 //   Phase 1 shifts over the dense lower-left rectangle (Q tiles >= n_q/2, KV
 //   tiles < n_kv/2), item p starting at the rectangle's Q tile p, its own
 //   index; phase 2 finishes column p upward and then column n_kv-1-p
-//   downward. Every item holds n_q + r tiles (zskr.cn 3.3,
+//   downward, each column one residue class of rows mod r after another (so a
+//   step's tiles stay inside one class; each dQ tile's order is that of plain
+//   upward and downward rows). Every item holds n_q + r tiles (zskr.cn 3.3,
 //   gist.science 2.2B; the fold itself is this library's reading, as the pages
 //   give no figure). The order is the step order.
 // * atomic (non-deterministic): ascending visits, unordered atomic adds.
