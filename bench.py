@@ -70,8 +70,14 @@ def strip_c_comments(text):
     return _C_TOKEN.sub(lambda m: "" if m.group(0).startswith("/") else m.group(0), text)
 
 
+def code_lines(text):
+    """The code of a C/C++ source: comments removed, then blank lines and
+    trailing blanks dropped, so a comment edit leaves it unchanged."""
+    return "\n".join(line.rstrip() for line in strip_c_comments(text).splitlines() if line.strip())
+
+
 def kernel_source_hash():
-    """sha256 over the HIP library sources with their comments removed (comments
+    """sha256 over the code of the HIP library sources (comments and blank lines
     never reach the binary): identifies the kernel build a profile was taken on."""
     import glob
     import hashlib
@@ -82,7 +88,7 @@ def kernel_source_hash():
     files.append(os.path.join(ROOT, "include", "detattn.h"))
     for f in files:
         h.update(os.path.basename(f).encode())
-        h.update(strip_c_comments(open(f).read()).encode())
+        h.update(code_lines(open(f).read()).encode())
     return h.hexdigest()
 
 

@@ -16,6 +16,14 @@ def test_profile_record_hash_ignores_comments_only():
     assert bench.strip_c_comments(src.replace("a = 1", "a = 2")) != out
 
 
+def test_code_lines_ignore_added_comment_lines():
+    src = "int f(int x) {\n  return x + 1;  // one\n}\n"
+    out = bench.code_lines(src)
+    assert bench.code_lines("// new line\n" + src.replace("// one", "// one\n  // two\n\n")) == out
+    assert bench.code_lines(src.replace("x + 1", "x + 2")) != out
+    assert out == "int f(int x) {\n  return x + 1;\n}"
+
+
 def test_kernel_source_hash_is_stable():
     h = bench.kernel_source_hash()
     assert len(h) == 64 and h == bench.kernel_source_hash()
