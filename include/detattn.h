@@ -63,7 +63,9 @@ typedef enum { DETATTN_MASK_FULL = 0, DETATTN_MASK_CAUSAL = 1 } detattn_mask_t;
  *  SYMMETRIC_SHIFT   causal mask only, even number of KV tiles: KV tiles p and
  *                    n-1-p share a workgroup; dense lower-left rectangle first
  *                    (item p starting at its Q tile p), then the folded
- *                    triangle (explainer 3.3; summary 2.2B).
+ *                    triangle (explainer 3.3; summary 2.2B): column p upward,
+ *                    then column n-1-p downward, each one residue class of
+ *                    rows mod r = block_kv / block_q after another.
  *  ATOMIC_NONDET     unordered fp32 atomic adds of the dQ partials: the
  *                    non-deterministic speed reference (explainer 2.1;
  *                    summary 1). dK and dV remain deterministic.
