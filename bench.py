@@ -257,7 +257,7 @@ def main():
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path",
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library has no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
 

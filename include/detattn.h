@@ -89,7 +89,7 @@ typedef enum {
 typedef enum {
   DETATTN_OK = 0,
   DETATTN_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad enum, negative size */
-  DETATTN_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement */
+  DETATTN_ERR_UNSUPPORTED = 2,   /* valid request this library does not implement */
   DETATTN_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
   DETATTN_ERR_HIP = 4,           /* a HIP runtime call failed (launch, copy, sync) */
   DETATTN_ERR_DEVICE_TIMEOUT = 5, /* an ordered dQ wait timed out on the device */
