@@ -9,8 +9,9 @@
 // goes straight from global memory to LDS by LDS-DMA). The D = 128
 // instances are held to 168 registers, three waves per SIMD, and the D = 64
 // ones to 128, four waves (the causal instances spill a few registers there
-// and are still faster than with fewer waves). Under a causal mask the grid
-// runs the query blocks with the most KV tiles first. Each wave computes the scores
+// and are still faster than with fewer waves). Under a causal mask the query
+// blocks with the most KV tiles run first, those of every head before any
+// lighter block. Each wave computes the scores
 // transposed, S^T = K Q^T, so that in the MFMA accumulator layout every lane
 // owns one query (its column) and the running max / sum of the online softmax
 // are per-lane scalars; O^T = V^T P^T then takes P^T straight from the
@@ -50,8 +51,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 
   __shared__ __attribute__((aligned(16))) __bf16 sK[C::BKV * C::P];
   __shared__ __attribute__((aligned(16))) __bf16 sV[C::BKV * C::P];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, c32 = lane & 31;
-  const int bh = blockIdx.y;
-  const int qb = CAUSAL ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;  // query block
+  // the grid is (head, query block) and workgroups are dispatched x-fastest,
+  // so under a causal mask every head's heaviest query block goes first
+  const int bh = blockIdx.x;
+  const int qb = CAUSAL ? (int)gridDim.y - 1 - (int)blockIdx.y : (int)blockIdx.y;  // query block
   const int q0 = qb * C::BQ + 32 * w;  // this wave's first query row
   const long long head = (long long)bh * S * D;
   const float c1 = scale * kLog2e;

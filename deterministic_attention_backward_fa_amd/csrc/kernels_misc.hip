@@ -105,7 +105,7 @@ hipError_t launch_main(const MainLaunch& L, hipStream_t st) {
 
 hipError_t launch_fwd(int D, int causal, const __bf16* q, const __bf16* k, const __bf16* v, __bf16* o, float* lse,
                       int BH, int S, float scale, hipStream_t st) {
-  dim3 grid((unsigned)(S / FwdCfg<64>::BQ), (unsigned)BH);
+  dim3 grid((unsigned)BH, (unsigned)(S / FwdCfg<64>::BQ));
   if (D == 64) {
     if (causal) fwd_kernel<64, true><<<grid, 256, 0, st>>>(q, k, v, o, lse, S, scale);
     else fwd_kernel<64, false><<<grid, 256, 0, st>>>(q, k, v, o, lse, S, scale);
