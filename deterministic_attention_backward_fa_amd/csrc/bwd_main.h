@@ -743,8 +743,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
         ring_bh += n_rings;
       }
     }
-    const int bh = gidx < 0 ? 0 : (int)(gidx / ipH);
-    const int it = gidx < 0 ? 0 : (int)(gidx % ipH);
+    // The ticket counter hands out the ordered schedules' items head-major, the
+    // greedy (head, KV tile) dispatch of the pages' DAG model. The unordered
+    // reference takes them item-major over the heads (every head's item 0,
+    // then every head's item 1, ...): under a causal mask its items shrink with
+    // the KV tile, so the longest go first across all heads. Rings: head-major.
+    int bh = 0, it = 0;
+    if (gidx >= 0) {
+      if (kUnordered && a.ticket_mode) {
+        it = (int)(gidx / a.BH);
+        bh = (int)(gidx % a.BH);
+      } else {
+        bh = (int)(gidx / ipH);
+        it = (int)(gidx % ipH);
+      }
+    }
     const long long head_off = (long long)bh * a.S * D;
     const long long bhS = (long long)bh * a.S;
     // the head's dQ accumulator as a buffer resource (32-bit offsets, range-checked)
