@@ -43,7 +43,12 @@ struct FwdCfg {
   static_assert(BKV * (NCH + 1) % 64 == 0 && P * 2 == (NCH + 1) * 16, "DMA tile layout");
 };
 
-template <int D, bool CAUSAL>
+// RAW_MAX (taken when scale * log2(e) is a positive normal float): the tile
+// maximum is found on the raw scores and scaled once. Rounding to nearest is
+// monotonic, so for a positive factor this is exactly the maximum of the
+// rounded products, one multiply per tile instead of one per score; the
+// exponent arguments are fma(s, c1, -m) either way.
+template <int D, bool CAUSAL, bool RAW_MAX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 3 : 4))) void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                                      const __bf16* __restrict__ v, __bf16* __restrict__ o,
                                                      float* __restrict__ lse, int S, float scale) {
@@ -133,13 +138,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 
     for (int mb = 0; mb < C::MK; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float x = sAcc[mb][r] * c1;
+        float x = RAW_MAX ? sAcc[mb][r] : sAcc[mb][r] * c1;
         const int kv = kv0 + 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
         if (diag && kv > qi) x = -INFINITY;
         sAcc[mb][r] = x;
         mx = fmaxf(mx, x);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if constexpr (RAW_MAX) mx *= c1;  // -inf (a fully masked tile) stays -inf
     const float m_new = fmaxf(m_run, mx);  // finite: key 0 is visible to every query
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     float lsum = 0.f;
@@ -148,7 +154,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 
     for (int mb = 0; mb < C::MK; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(sAcc[mb][r] - m_new);
+        const float p = __builtin_amdgcn_exp2f(RAW_MAX ? __builtin_fmaf(sAcc[mb][r], c1, -m_new) : sAcc[mb][r] - m_new);
         const __bf16 pb = (__bf16)p;
         lsum += p;
         pB[2 * mb + (r >> 3)][r & 7] = pb;

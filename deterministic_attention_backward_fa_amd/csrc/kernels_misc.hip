@@ -1,6 +1,9 @@
 // Launchers of the preprocess, convert and forward kernels, and of the main
 // backward kernel (plain or cooperative grid).
 #include "fwd_kernels.h"
+
+#include <cfloat>
+
 #include "launch.h"
 
 namespace detattn {
@@ -106,12 +109,16 @@ hipError_t launch_main(const MainLaunch& L, hipStream_t st) {
 hipError_t launch_fwd(int D, int causal, const __bf16* q, const __bf16* k, const __bf16* v, __bf16* o, float* lse,
                       int BH, int S, float scale, hipStream_t st) {
   dim3 grid((unsigned)BH, (unsigned)(S / FwdCfg<64>::BQ));
+  // the kernel's own factor, computed the same way: the raw-score maximum
+  // needs it positive and normal (any scale > 0 that does not overflow)
+  const float c1 = scale * kLog2e;
+  const bool raw = c1 >= FLT_MIN && c1 <= FLT_MAX;
   if (D == 64) {
-    if (causal) fwd_kernel<64, true><<<grid, 256, 0, st>>>(q, k, v, o, lse, S, scale);
-    else fwd_kernel<64, false><<<grid, 256, 0, st>>>(q, k, v, o, lse, S, scale);
+    if (causal) (raw ? fwd_kernel<64, true, true> : fwd_kernel<64, true, false>)<<<grid, 256, 0, st>>>(q, k, v, o, lse, S, scale);
+    else (raw ? fwd_kernel<64, false, true> : fwd_kernel<64, false, false>)<<<grid, 256, 0, st>>>(q, k, v, o, lse, S, scale);
   } else {
-    if (causal) fwd_kernel<128, true><<<grid, 256, 0, st>>>(q, k, v, o, lse, S, scale);
-    else fwd_kernel<128, false><<<grid, 256, 0, st>>>(q, k, v, o, lse, S, scale);
+    if (causal) (raw ? fwd_kernel<128, true, true> : fwd_kernel<128, true, false>)<<<grid, 256, 0, st>>>(q, k, v, o, lse, S, scale);
+    else (raw ? fwd_kernel<128, false, true> : fwd_kernel<128, false, false>)<<<grid, 256, 0, st>>>(q, k, v, o, lse, S, scale);
   }
   return hipGetLastError();
 }

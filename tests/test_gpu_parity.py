@@ -61,6 +61,20 @@ def test_forward_matches_oracle(case):
     assert np.max(np.abs(lse.cpu().numpy() - lse_ref)) <= 1e-3
 
 
+@pytest.mark.parametrize("scale", [1.0, 0.0, -0.3])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_other_scales_match_oracle(scale, D, causal):
+    # a positive scale takes the instance that finds the tile maximum on the raw
+    # scores; zero and negative scales take the one that scales every score first
+    B, H, S = 1, 2, 384
+    say(f"[fwd scale] scale={scale} D={D} causal={causal}")
+    cpu, (q, k, v, do, o, lse) = inputs(B, H, S, D, 19, causal, scale=scale)
+    o_ref, lse_ref = oref.attn_fwd(cpu[0], cpu[1], cpu[2], scale, causal)
+    assert rel_err(o.float().cpu().numpy(), o_ref) <= TOL
+    assert np.max(np.abs(lse.cpu().numpy() - lse_ref)) <= 1e-3
+
+
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: f"B{c[0]}H{c[1]}S{c[2]}D{c[3]}{'c' if c[4] else 'f'}")
 def test_backward_matches_oracle_all_schedules(case):
     B, H, S, D, causal, seed, opts = case
